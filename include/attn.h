@@ -1,0 +1,163 @@
+/*
+ * attn.h -- C ABI of a BF16 fused softmax-attention library for AMD MI355X
+ * (gfx950), with the duplicate-max ("stabilised") safe softmax as a
+ * switchable mode.
+ *
+ * The method (web pages on Qiu & Yao, "Why Low-Precision Transformer Training
+ * Fails: An Analysis on Flash Attention", arXiv 2510.04212):
+ *   - itsolotime.com/archives/23922, section "机制解释二" (origin of the bias):
+ *     the forward forms P_bar = exp(S - m), P = P_bar / rowsum(P_bar),
+ *     O = P V; when a row of S reaches its maximum more than once, P_bar holds
+ *     several entries exactly equal to 1, the trigger of the bias.
+ *   - same page, section "极简修复方案" (minimal fix): count how often the row
+ *     maximum rm occurs (rs); when rs > 1 the shift becomes beta * rm for
+ *     rm > 0 (beta > 1) or 0 for rm < 0, otherwise it stays rm, so the largest
+ *     P_bar entry of a repeated-max row falls below 1; softmax is unchanged by
+ *     a per-row shift in exact arithmetic.
+ *   - 91haoming.cn/news/show-608006, section 三: the backward's delta is the
+ *     row-sum of an element-wise product, delta_i = sum_c dO_ic O_ic, and the
+ *     backward forms dP.
+ *
+ * Conventions shared by every entry point
+ *   Layout   q, k, v, o, dO, dq, dk, dv are bf16 (IEEE bfloat16 bits: 1 sign,
+ *            8 exponent, 7 fraction bits), contiguous row-major [B][H][N][D];
+ *            self-attention, the same N for queries and keys.  Per-row vectors
+ *            (lse, delta, ties, ...) are contiguous [B][H][N].  All pointers
+ *            are device pointers, 16-byte aligned.
+ *   Causal   query i sees keys j <= i (top-left aligned); otherwise all N keys.
+ *   Scores   S_ij = scale * (q_i . k_j); scale must be finite and > 0.  The
+ *            duplicate test compares the raw fp32 dot products q_i . k_j as
+ *            the kernel forms them (bf16 MFMA, fp32 accumulation); with
+ *            scale > 0 this is the same order as S.
+ *   Shapes   B, H, N >= 0 (B*H*N == 0 is a no-op returning ATTN_OK); any
+ *            N >= 1 (ragged tiles are masked); D in {64, 128}; B*H*N*D below
+ *            2^31 elements per tensor.
+ *   Ownership  The caller allocates and owns every buffer.  The library never
+ *            allocates, frees or synchronises; it keeps no state between calls
+ *            except a per-device cache of the device's architecture.  Inputs
+ *            are read only; outputs are fully overwritten; no output may
+ *            overlap an input or another output.
+ *   Errors   Arguments are validated before any HIP call; on error nothing is
+ *            launched and a negative attn_status is returned.  A device that
+ *            is not gfx950, or a failed launch, returns ATTN_E_DEVICE.  Work
+ *            is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *            stream), so faults surface at the caller's next synchronisation.
+ *            No C++ exception crosses this interface.
+ */
+#ifndef NSS_ATTN_H
+#define NSS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_NULLPTR = -1,   /* a required pointer is NULL                          */
+  ATTN_E_SHAPE = -2,     /* B, H or N negative, or a tensor too large           */
+  ATTN_E_HEADDIM = -3,   /* D not in {64, 128}                                  */
+  ATTN_E_BETA = -4,      /* stabilise != 0 and beta not finite or not > 1       */
+  ATTN_E_SCALE = -5,     /* scale not finite or not > 0                         */
+  ATTN_E_ALIGN = -6,     /* a pointer is not 16-byte aligned                    */
+  ATTN_E_ALIAS = -7,     /* an output overlaps an input or another output       */
+  ATTN_E_DEVICE = -9     /* not a gfx950 device, or a HIP launch failed         */
+} attn_status;
+
+/*
+ * attn_fwd -- fused attention forward with the online (max, count) merge.
+ *
+ * Computes, per row i and over its visible keys, S = scale * q_i . k_j, the
+ * row maximum rm and how many keys reach it rs (merged across KV tiles as a
+ * (max, count) pair: the larger max keeps its count, equal maxima add), the
+ * shift m (stabilise == 0: m = rm; stabilise != 0: the rule of
+ * itsolotime.com/archives/23922, section "极简修复方案"), P_bar = exp(S - m),
+ * O = (P_bar V) / rowsum(P_bar) and LSE = m + ln rowsum(P_bar)
+ * (section "机制解释二" of the same page).  The shift is applied online: while a
+ * tile is processed, m comes from the running (max, count).  P_bar is formed
+ * in fp32 and rounded to bf16 (nearest even) as the operand of P_bar V; the
+ * row sum adds the fp32 values.
+ *
+ *   q, k, v      in   bf16 [B][H][N][D]
+ *   o            out  bf16 [B][H][N][D]
+ *   lse          out  fp32 [B][H][N], natural-log log-sum-exp of S (the
+ *                     backward's input)
+ *   ties         out  int32 [B][H][N] or NULL: rs, the final duplicate count
+ *   pbar_one     out  int32 [B][H][N] or NULL: 1 when the largest entry of the
+ *                     final-shift P_bar, exp(rm - m), rounds (bf16, nearest
+ *                     even) to exactly 1.0, else 0
+ *   formed_ones  out  int32 [B][H][N] or NULL: how many bf16 P_bar operands
+ *                     equal to 1.0 the kernel actually fed to P_bar V (a tie
+ *                     split across KV tiles forms one before its duplicate is
+ *                     seen)
+ *   stabilise    0 = plain safe softmax, 1 = duplicate-max shift
+ *   beta         the rule's factor (> 1, finite) when stabilise != 0; ignored
+ *                otherwise
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int32_t* ties, int32_t* pbar_one, int32_t* formed_ones,
+             int B, int H, int N, int D, float scale, int causal, int stabilise,
+             float beta, void* stream);
+
+/*
+ * attn_bwd -- gradient of sum(dO * O) with respect to q, k and v.
+ *
+ * Runs attn_bwd_dq then attn_bwd_dkdv on `stream`.  With P = exp(S - lse):
+ * delta_i = sum_c dO_ic O_ic (91haoming.cn/news/show-608006, section 三),
+ * dP = dO V^T, dS = P o (dP - delta), dQ = scale dS K, dK = scale dS^T Q,
+ * dV = P^T dO.  P is recomputed from the forward's lse, which carries the
+ * forward's shift, so the arithmetic is the same in both modes; `stabilise`
+ * and `beta` are validated as for attn_fwd and otherwise unused.
+ *
+ *   q, k, v, o, dO  in   bf16 [B][H][N][D] (o from attn_fwd)
+ *   lse             in   fp32 [B][H][N] from attn_fwd
+ *   dq, dk, dv      out  bf16 [B][H][N][D]
+ *   delta           out  fp32 [B][H][N]: rowsum(dO o O), kept for the caller
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv, float* delta,
+             int B, int H, int N, int D, float scale, int causal, int stabilise,
+             float beta, void* stream);
+
+/*
+ * attn_bwd_dq -- first half of attn_bwd: delta and dQ, one pass per query
+ * tile over its visible keys.  Arguments as attn_bwd.
+ */
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, void* dq, float* delta,
+                int B, int H, int N, int D, float scale, int causal, void* stream);
+
+/*
+ * attn_bwd_dkdv -- second half of attn_bwd: dK and dV, one pass per key tile
+ * over the queries that see it.  `delta` is read (attn_bwd_dq's output).
+ */
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                  const float* lse, const float* delta, void* dk, void* dv,
+                  int B, int H, int N, int D, float scale, int causal, void* stream);
+
+/*
+ * attn_tiecount -- the duplicate-max detector alone
+ * (itsolotime.com/archives/23922, section "极简修复方案": whether, and how
+ * often, the maximum of a row of S repeats).
+ *
+ *   q, k     in   bf16 [B][H][N][D]
+ *   ties     out  int32 [B][H][N]: rs over the visible keys
+ *   rowmax   out  fp32 [B][H][N] or NULL: rm = scale * max_j (q_i . k_j),
+ *                 the fp32 product of scale and the raw fp32 maximum
+ */
+int attn_tiecount(const void* q, const void* k, int32_t* ties, float* rowmax,
+                  int B, int H, int N, int D, float scale, int causal, void* stream);
+
+/* Static, human-readable text for an attn_status value. */
+const char* attn_status_string(int status);
+
+/* ABI version of this header (incremented on any signature change). */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSS_ATTN_H */

@@ -1,0 +1,12 @@
+"""BF16 fused attention for AMD MI355X (gfx950) with the duplicate-max
+stabilised safe softmax as a switchable mode.
+
+The compute lives in libattn.so (hand-written HIP, C ABI in include/attn.h);
+``binding`` marshals torch tensors to it; ``inputs`` generates the seeded
+synthetic workloads.
+"""
+from .binding import (AttnError, abi_version, attn_bwd, attn_bwd_dkdv, attn_bwd_dq, attn_fwd,
+                      attn_tiecount, backward, forward, status_string, tiecount)
+
+__all__ = ["AttnError", "abi_version", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd",
+           "attn_tiecount", "backward", "forward", "status_string", "tiecount"]

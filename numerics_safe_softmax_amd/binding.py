@@ -1,0 +1,168 @@
+"""ctypes binding of libattn.so (include/attn.h): argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, passes their
+data pointers, shapes and the current HIP stream to the C entry point of the
+same name, and raises AttnError on a non-zero status.  All arithmetic runs in
+the library's gfx950 kernels; there is no fallback path.  If libattn.so has
+not been built, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "attn.h")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+_SIGS = {
+    "attn_fwd": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _F, _P],
+    "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _F, _P],
+    "attn_bwd_dq": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P],
+    "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P],
+    "attn_tiecount": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P],
+    "attn_status_string": [_I],
+    "attn_abi_version": [],
+}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__("attn status %d: %s" % (status, text))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libattn.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libattn.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_char_p if name == "attn_status_string" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/attn.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().attn_abi_version())
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise AttnError(rc, status_string(rc))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the C ABI must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, D]")
+    return tuple(int(x) for x in q.shape)
+
+
+def attn_fwd(q, k, v, o, lse, ties=None, pbar_one=None, formed_ones=None, *, scale: float,
+             causal: bool, stabilise: bool, beta: float = 2.0, stream=None) -> None:
+    B, H, N, D = _shape(q)
+    _check(lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ties), _ptr(pbar_one),
+                          _ptr(formed_ones), B, H, N, D, float(scale), int(bool(causal)),
+                          int(bool(stabilise)), float(beta), _stream(stream)))
+
+
+def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, *, scale: float, causal: bool, stabilise: bool,
+             beta: float = 2.0, stream=None) -> None:
+    B, H, N, D = _shape(q)
+    _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(delta), B, H, N, D, float(scale), int(bool(causal)),
+                          int(bool(stabilise)), float(beta), _stream(stream)))
+
+
+def attn_bwd_dq(q, k, v, o, dO, lse, dq, delta, *, scale: float, causal: bool, stream=None) -> None:
+    B, H, N, D = _shape(q)
+    _check(lib().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq),
+                             _ptr(delta), B, H, N, D, float(scale), int(bool(causal)), _stream(stream)))
+
+
+def attn_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, *, scale: float, causal: bool, stream=None) -> None:
+    B, H, N, D = _shape(q)
+    _check(lib().attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(dk),
+                               _ptr(dv), B, H, N, D, float(scale), int(bool(causal)), _stream(stream)))
+
+
+def attn_tiecount(q, k, ties, rowmax=None, *, scale: float, causal: bool, stream=None) -> None:
+    B, H, N, D = _shape(q)
+    _check(lib().attn_tiecount(_ptr(q), _ptr(k), _ptr(ties), _ptr(rowmax), B, H, N, D, float(scale),
+                               int(bool(causal)), _stream(stream)))
+
+
+# ------------------------------------------------------------- conveniences
+# Allocation of outputs with torch, then one call of the entry point above.
+
+def forward(q, k, v, *, scale: float, causal: bool, stabilise: bool, beta: float = 2.0,
+            diagnostics: bool = True, stream=None) -> dict:
+    import torch
+    B, H, N, D = _shape(q)
+    dev = q.device
+    out = {"o": torch.empty_like(q), "lse": torch.empty((B, H, N), dtype=torch.float32, device=dev)}
+    if diagnostics:
+        for f in ("ties", "pbar_one", "formed_ones"):
+            out[f] = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    attn_fwd(q, k, v, out["o"], out["lse"], out.get("ties"), out.get("pbar_one"), out.get("formed_ones"),
+             scale=scale, causal=causal, stabilise=stabilise, beta=beta, stream=stream)
+    return out
+
+
+def backward(q, k, v, o, dO, lse, *, scale: float, causal: bool, stabilise: bool = False,
+             beta: float = 2.0, stream=None) -> dict:
+    import torch
+    B, H, N, D = _shape(q)
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(q), "dv": torch.empty_like(q),
+           "delta": torch.empty((B, H, N), dtype=torch.float32, device=q.device)}
+    attn_bwd(q, k, v, o, dO, lse, out["dq"], out["dk"], out["dv"], out["delta"], scale=scale,
+             causal=causal, stabilise=stabilise, beta=beta, stream=stream)
+    return out
+
+
+def tiecount(q, k, *, scale: float, causal: bool, stream=None) -> dict:
+    import torch
+    B, H, N, D = _shape(q)
+    out = {"ties": torch.empty((B, H, N), dtype=torch.int32, device=q.device),
+           "rowmax": torch.empty((B, H, N), dtype=torch.float32, device=q.device)}
+    attn_tiecount(q, k, out["ties"], out["rowmax"], scale=scale, causal=causal, stream=stream)
+    return out

@@ -1,0 +1,36 @@
+// attn_launch.h -- internal interface between the C ABI (attn_abi.hip) and the
+// gfx950 kernels (attn_kernels.hip).  Arguments arrive here validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nss {
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  int32_t *ties, *pbar_one, *formed_ones;
+  float* rowmax;
+  int B, H, N, D;
+  float scale;
+  int causal, stabilise;
+  float beta;
+};
+
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dO;
+  const float* lse;
+  void *dq, *dk, *dv;
+  float* delta;
+  int B, H, N, D;
+  float scale;
+  int causal;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
+hipError_t launch_tiecount(const FwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st);
+
+}  // namespace nss

@@ -1,0 +1,79 @@
+"""Shared helpers of the GPU parity tests: run the C-ABI path on seeded inputs
+and compare it element by element with the FP64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from numerics_safe_softmax_amd import inputs
+
+FWD_WANT = ["O", "tol_O", "lse", "tol_lse", "ties", "pbar_one", "amb_tie", "amb_pbar", "near_ones",
+            "rowmax", "flags"]
+
+
+def to_dev(d, dev):
+    return {k: inputs.to_torch(v, dev) for k, v in d.items()}
+
+
+def f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def gpu_forward(t, w, stabilise):
+    import numerics_safe_softmax_amd as nss
+    return nss.forward(t["q"], t["k"], t["v"], scale=w.scale, causal=w.causal, stabilise=stabilise,
+                       beta=w.beta)
+
+
+def gpu_backward(t, w, f, stabilise):
+    import numerics_safe_softmax_amd as nss
+    return nss.backward(t["q"], t["k"], t["v"], f["o"], t["dO"], f["lse"], scale=w.scale,
+                        causal=w.causal, stabilise=stabilise, beta=w.beta)
+
+
+def ratio(got, want, tol, mask=None):
+    """Largest |got - want| / tol over the (optionally masked) elements."""
+    r = np.abs(got - want) / tol
+    if mask is not None:
+        r = r[mask]
+    return float(np.max(r)) if r.size else 0.0
+
+
+def check_forward(f, ref, rows_mask=None, label=""):
+    """O and LSE within tolerance; ties and pbar_one bit-exact off the ambiguous rows."""
+    m = np.ones(ref["lse"].shape, dtype=bool) if rows_mask is None else rows_mask
+    O = f64(f["o"])
+    lse = f64(f["lse"])
+    rO = ratio(O, ref["O"], ref["tol_O"], m[..., None].repeat(O.shape[-1], axis=-1))
+    rL = ratio(lse, ref["lse"], ref["tol_lse"], m)
+    assert rO <= 1.0, "%s O max err/tol %.3f" % (label, rO)
+    assert rL <= 1.0, "%s LSE max err/tol %.3f" % (label, rL)
+    ok = m & (ref["amb_tie"] == 0)
+    ties = f["ties"].cpu().numpy()
+    bad = int(np.sum(ties[ok] != ref["ties"][ok]))
+    assert bad == 0, "%s %d tie-count mismatches" % (label, bad)
+    okp = ok & (ref["amb_pbar"] == 0)
+    pone = f["pbar_one"].cpu().numpy()
+    badp = int(np.sum(pone[okp] != ref["pbar_one"][okp]))
+    assert badp == 0, "%s %d pbar_one mismatches" % (label, badp)
+    return {"O": rO, "LSE": rL, "ambiguous_rows": int(np.sum(m & (ref["amb_tie"] != 0)))}
+
+
+def check_backward(b, rb, heads=None, label=""):
+    B, H, N, D = rb["dQ"].shape
+    hm = np.zeros((B, H), dtype=bool)
+    if heads is None:
+        hm[:] = True
+    else:
+        for x in heads:
+            hm[x // H, x % H] = True
+    out = {}
+    for name, key in (("dq", "dQ"), ("dk", "dK"), ("dv", "dV")):
+        got = f64(b[name])
+        r = ratio(got[hm], rb[key][hm], rb["tol_" + key][hm])
+        assert r <= 1.0, "%s %s max err/tol %.3f" % (label, key, r)
+        out[key] = r
+    r = ratio(f64(b["delta"])[hm], rb["delta"][hm], rb["tol_delta"][hm])
+    assert r <= 1.0, "%s delta max err/tol %.3f" % (label, r)
+    out["delta"] = r
+    return out

@@ -1,0 +1,145 @@
+"""GPU parity: the C-ABI HIP path against the FP64 oracle, element by element.
+
+Small shapes span several 128-row workgroup tiles and 64-key tiles with a
+ragged tail, in both modes, causal and not, for D = 64 and 128; the full-size
+workloads are checked on sampled rows and heads in the launch configuration the
+benchmark times.  Integers (duplicate counts, P_bar == 1 flags) must match
+exactly off the rows the oracle marks as undecidable in fp32.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from numerics_safe_softmax_amd import inputs
+from tests import parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+SMALL = [
+    # (B, H, N, D, causal, seed, tie_block)
+    (1, 2, 200, 64, True, 11, 5),
+    (2, 1, 333, 64, False, 12, 0),
+    (1, 2, 300, 128, True, 13, 6),
+    (1, 1, 130, 128, False, 14, 0),
+    (1, 3, 1000, 64, True, 15, 10),
+    (1, 1, 65, 64, True, 16, 4),
+    (1, 1, 1, 64, True, 17, 0),
+    (1, 1, 1, 128, False, 18, 0),
+    (1, 1, 64, 128, True, 19, 4),
+]
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _small_workload(B, H, N, D, causal, seed, tie_block):
+    return inputs.custom("parity", B, H, N, D, causal, seed, tie_block=tie_block,
+                         v_skew_dims=D // 4, v_mu=-2.0, v_sigma=0.5, do_mu=-0.5)
+
+
+@pytest.mark.parametrize("stabilise", [False, True])
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dH%dN%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
+def test_small_fwd_bwd_parity(case, stabilise):
+    w = _small_workload(*case)
+    _say("parity %s stabilise=%d" % (case, stabilise))
+    d = inputs.generate(w)
+    t = parity.to_dev(d, DEV)
+    f = parity.gpu_forward(t, w, stabilise)
+    b = parity.gpu_backward(t, w, f, stabilise)
+    torch.cuda.synchronize()
+    ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=stabilise,
+                         beta=w.beta)
+    rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=w.causal)
+    fr = parity.check_forward(f, ref, label=str(case))
+    br = parity.check_backward(b, rb, label=str(case))
+    _say("  fwd %s bwd %s" % (fr, br))
+    # unstabilised rows: each tied maximum is fed to P_bar V as an exact bf16 1.0
+    formed = f["formed_ones"].cpu().numpy()
+    ok = ref["amb_tie"] == 0
+    if not stabilise:
+        assert np.all(formed[ok] >= ref["ties"][ok])
+        assert np.all(f["pbar_one"].cpu().numpy() == 1)
+
+
+@pytest.mark.parametrize("case", SMALL[:5], ids=lambda c: "B%dH%dN%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
+def test_tiecount_parity(case):
+    import numerics_safe_softmax_amd as nss
+    w = _small_workload(*case)
+    d = inputs.generate(w)
+    t = parity.to_dev(d, DEV)
+    r = nss.tiecount(t["q"], t["k"], scale=w.scale, causal=w.causal)
+    f = parity.gpu_forward(t, w, True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(d["q"], d["k"], scale=w.scale, causal=w.causal,
+                         want=["ties", "amb_tie", "rowmax"])
+    ok = ref["amb_tie"] == 0
+    ties = r["ties"].cpu().numpy()
+    assert np.array_equal(ties[ok], ref["ties"][ok])
+    # the detector and the forward form the same fp32 scores: identical counts everywhere
+    assert np.array_equal(ties, f["ties"].cpu().numpy())
+    rm = r["rowmax"].cpu().numpy().astype(np.float64)
+    assert np.allclose(rm, ref["rowmax"], rtol=2e-6, atol=1e-6)
+
+
+def test_deterministic_reruns():
+    w = _small_workload(2, 2, 700, 64, True, 21, 7)
+    d = inputs.generate(w)
+    t = parity.to_dev(d, DEV)
+    outs = []
+    for _ in range(2):
+        f = parity.gpu_forward(t, w, True)
+        b = parity.gpu_backward(t, w, f, True)
+        torch.cuda.synchronize()
+        outs.append({k: v.cpu().clone() for k, v in list(f.items()) + list(b.items())})
+    for k in outs[0]:
+        assert torch.equal(outs[0][k].view(torch.uint8) if outs[0][k].dtype == torch.bfloat16 else outs[0][k],
+                           outs[1][k].view(torch.uint8) if outs[1][k].dtype == torch.bfloat16 else outs[1][k]), k
+
+
+def test_empty_problems_are_no_ops():
+    import numerics_safe_softmax_amd as nss
+    for shape in [(0, 2, 16, 64), (1, 0, 16, 64), (1, 2, 0, 64)]:
+        q = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+        f = nss.forward(q, q.clone(), q.clone(), scale=0.125, causal=True, stabilise=True)
+        b = nss.backward(q, q.clone(), q.clone(), f["o"], q.clone(), f["lse"], scale=0.125, causal=True)
+        assert f["o"].numel() == 0 and b["dq"].numel() == 0
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("wname,heads", [("tiny", [0]), ("gpt2_small", [0, 57, 95]),
+                                          ("gpt2_medium", [5, 127]), ("sink", [0, 30]),
+                                          ("long_context", [9])])
+def test_workload_parity(wname, heads):
+    """Full-size workloads in the launch configuration the benchmark times; the
+    oracle computes every row of the sampled heads (forward and backward)."""
+    w = inputs.WORKLOADS[wname]
+    _say("workload %s heads %s" % (wname, heads))
+    d = inputs.generate(w)
+    t = parity.to_dev(d, DEV)
+    rows = oracle.head_rows(heads, w.N)
+    hm = np.zeros((w.B, w.H), dtype=bool)
+    for x in heads:
+        hm[x // w.H, x % w.H] = True
+    rmask = np.repeat(hm[:, :, None], w.N, axis=2)
+    for stabilise in (False, True):
+        f = parity.gpu_forward(t, w, stabilise)
+        b = parity.gpu_backward(t, w, f, stabilise)
+        torch.cuda.synchronize()
+        ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal,
+                             stabilise=stabilise, beta=w.beta, rows=rows, want=parity.FWD_WANT)
+        fr = parity.check_forward(f, ref, rows_mask=rmask, label="%s s=%d" % (wname, stabilise))
+        rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=w.causal,
+                             heads=heads)
+        br = parity.check_backward(b, rb, heads=heads, label="%s s=%d" % (wname, stabilise))
+        tie = rmask & (ref["ties"] > 1)
+        _say("  s=%d fwd %s bwd %s tie rows %d" % (stabilise, fr, br, int(tie.sum())))
+        if stabilise:
+            ok = tie & (ref["amb_tie"] == 0) & (ref["amb_pbar"] == 0) & ((ref["flags"] & 1) == 0)
+            assert np.all(f["pbar_one"].cpu().numpy()[ok] == 0)
