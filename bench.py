@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Throughput of the stabilised BF16 attention hot path on one MI355X.
+
+A step is one pass of the whole path over the GPT-2-small attention layer
+(B=8, H=12, N=1024, D=64, causal, bf16, synthetic seeded inputs with
+duplicate-max rows): attn_fwd (duplicate-max shift on, with its tie, P_bar == 1
+and formed-ones outputs) followed by attn_bwd (attn_bwd_dq then attn_bwd_dkdv).
+Inputs are resident in HBM before the timed region.  The reported value is
+algorithmic fwd+bwd TFLOPS (4 D + 10 D flops per visible query-key pair).
+
+Printed: ONE JSON line with the metric, per-kernel HIP-event timings, the
+roofline of the dominant kernel and the FP64 oracle timed on the host (the
+cpu_baseline leg, which also yields the signed-bias diagnostic against FP64).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOPS (bf16) at GPT-2 shape; % of MFMA peak; O/dP signed bias"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk/CU x 2.4 GHz, dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "numerics_safe_softmax_amd", "csrc", "attn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2_small.md")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="gpt2_small")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the host oracle leg (profiling runs)")
+    return p.parse_args()
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel source changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != kernel_hash():
+        return None
+    m = re.search(r"^%s_bytes_per_launch:\s*([0-9.eE+]+)" % re.escape(kernel), text, re.M)
+    return float(m.group(1)) if m else None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(attention heads shard across GPUs with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import numerics_safe_softmax_amd as nss
+    from numerics_safe_softmax_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[args.workload]
+    B, H, N, D = w.B, w.H, w.N, w.D
+    d = inputs.generate(w)
+    t = {k: inputs.to_torch(v, dev) for k, v in d.items()}
+    q, k, v, g = t["q"], t["k"], t["v"], t["dO"]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ties, pone, formed = (torch.empty((B, H, N), dtype=torch.int32, device=dev) for _ in range(3))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    kw = dict(scale=w.scale, causal=w.causal)
+
+    def fwd(stabilise=True):
+        nss.attn_fwd(q, k, v, o, lse, ties, pone, formed, stabilise=stabilise, beta=w.beta, stream=stream, **kw)
+
+    def bwd_dq():
+        nss.attn_bwd_dq(q, k, v, o, g, lse, dq, delta, stream=stream, **kw)
+
+    def bwd_dkdv():
+        nss.attn_bwd_dkdv(q, k, v, g, lse, delta, dk, dv, stream=stream, **kw)
+
+    def step():
+        fwd()
+        bwd_dq()
+        bwd_dkdv()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step wall clock over exactly K steps
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-kernel HIP events on the launch stream (separate pass of K steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        fwd()
+        ev[s][1].record(stream)
+        bwd_dq()
+        ev[s][2].record(stream)
+        bwd_dkdv()
+        ev[s][3].record(stream)
+    torch.cuda.synchronize()
+    per = {"fwd": [], "bwd_dq": [], "bwd_dkdv": []}
+    for s in range(args.steps):
+        per["fwd"].append(ev[s][0].elapsed_time(ev[s][1]))
+        per["bwd_dq"].append(ev[s][1].elapsed_time(ev[s][2]))
+        per["bwd_dkdv"].append(ev[s][2].elapsed_time(ev[s][3]))
+    us = {k2: float(np.mean(x)) * 1e3 for k2, x in per.items()}
+
+    # the plain (unstabilised) forward for comparison
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fwd(stabilise=False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_plain_us = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    fwd_flops, bwd_flops = w.fwd_flops(), w.bwd_flops()
+    pairs = w.visible_pairs()
+    tflops = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
+
+    # algorithmic work of each kernel per launch (flops, compulsory HBM bytes)
+    tb = B * H * N * D * 2
+    rb = B * H * N * 4
+    kinfo = {
+        # S = QK^T and P_bar V: 4 D flops per visible pair; reads Q, K, V, writes O, LSE, 3 int rows
+        "fwd": (4.0 * D * pairs, 4 * tb + 4 * rb),
+        # dQ = scale dS K: 2 D per pair (its S / dP recompute is overhead of the split);
+        # reads Q, K, V, O, dO, LSE, writes dQ, delta
+        "bwd_dq": (2.0 * D * pairs, 6 * tb + 2 * rb),
+        # S recompute, dP, dV, dK: 8 D per pair; reads Q, K, V, dO, LSE, delta, writes dK, dV
+        "bwd_dkdv": (8.0 * D * pairs, 6 * tb + 2 * rb),
+    }
+    dom = max(us, key=lambda x: us[x])
+    flops_dom, bytes_dom = kinfo[dom]
+    achieved = flops_dom / (us[dom] * 1e-6) / 1e12
+    traffic = measured_traffic(dom)
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "algorithmic_bytes": bytes_dom, "avg_launch_us": us[dom]}
+
+    out = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "D": D, "causal": w.causal,
+                   "stabilise": True, "beta": w.beta, "global_batch": B, "seq_len": N,
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "peak_assumption": "2516.6 TFLOPS dense bf16 = 256 CU x 4096 flop/clk x 2.4 GHz",
+        "kernels_us": us,
+        "fwd_us": us["fwd"],
+        "bwd_us": us["bwd_dq"] + us["bwd_dkdv"],
+        "fwd_tflops": fwd_flops / (us["fwd"] * 1e-6) / 1e12,
+        "bwd_tflops": bwd_flops / ((us["bwd_dq"] + us["bwd_dkdv"]) * 1e-6) / 1e12,
+        "fwd_unstabilised_us": fwd_plain_us,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"], out["bias"] = cpu_leg(w, d, nss, t, stream)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_leg(w, d, nss, t, stream):
+    """The FP64 oracle on the host, on the whole workload (fwd + bwd), timed;
+    its result also gives the signed-bias diagnostic of both GPU modes."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle import bias
+
+    t0 = time.perf_counter()
+    ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=True,
+                         beta=w.beta, want=["O", "tol_O", "lse", "tol_lse", "ties"])
+    t1 = time.perf_counter()
+    rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=w.causal)
+    t2 = time.perf_counter()
+    cores = oracle.threads()
+    flops = w.fwd_flops() + w.bwd_flops()
+    cpu = {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+           "sample": "the whole %s workload (B=%d H=%d N=%d D=%d), FP64 forward + backward, "
+                     "%.2f s + %.2f s" % (w.name, w.B, w.H, w.N, w.D, t1 - t0, t2 - t1),
+           "seconds": t2 - t0}
+
+    gO = inputs_f64(d["dO"])
+    res = {}
+    for stabilise in (False, True):
+        f = nss.forward(t["q"], t["k"], t["v"], scale=w.scale, causal=w.causal, stabilise=stabilise,
+                        beta=w.beta, stream=stream)
+        b = nss.backward(t["q"], t["k"], t["v"], f["o"], t["dO"], f["lse"], scale=w.scale,
+                         causal=w.causal, stabilise=stabilise, beta=w.beta, stream=stream)
+        torch.cuda.synchronize()
+        O = f["o"].float().cpu().numpy().astype(np.float64)
+        dl = b["delta"].cpu().numpy().astype(np.float64)
+        rep = bias.report(O, ref["O"], dl, rb["delta"], gO, ref["ties"],
+                          np.ones(ref["ties"].shape, dtype=bool), w.v_skew_dims)
+        rep["max_err_over_tol"] = {
+            "O": float(np.max(np.abs(O - ref["O"]) / ref["tol_O"])),
+            "delta": float(np.max(np.abs(dl - rb["delta"]) / rb["tol_delta"]))}
+        rep["pbar_one_events_on_tie_rows"] = int(f["pbar_one"].cpu().numpy()[ref["ties"] > 1].sum())
+        rep["formed_ones_on_tie_rows"] = int(f["formed_ones"].cpu().numpy()[ref["ties"] > 1].sum())
+        res["stabilised" if stabilise else "unstabilised"] = rep
+    res["O_mode_difference_z"] = bias.mode_difference(res["stabilised"]["O_tie_rows_skewed_dims"],
+                                                      res["unstabilised"]["O_tie_rows_skewed_dims"])
+    res["tie_rows"] = int((ref["ties"] > 1).sum())
+    return cpu, res
+
+
+def inputs_f64(bits):
+    from numerics_safe_softmax_amd import inputs
+    return inputs.bits_to_float(bits).astype("float64")
+
+
+if __name__ == "__main__":
+    main()

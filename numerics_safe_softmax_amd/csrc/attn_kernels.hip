@@ -12,22 +12,27 @@
 // Design (MI355X-first, not a port of the pages' GPU design):
 //   * one wave64 owns 32 rows; every dense contraction is a chain of
 //     v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32 accumulation);
-//   * the score tile is formed TRANSPOSED where a row statistic is needed
-//     (keys on the MFMA row axis, the 32 queries on the lane axis), so the row
-//     max, the duplicate count and the row sum are in-lane reductions plus one
-//     exchange between the two 32-lane halves;
+//   * the score tile is formed with the 32 rows of the wave on the lane axis,
+//     so the row max, the duplicate count and the row sum are in-lane
+//     reductions plus one exchange between the two 32-lane halves;
 //   * the fp32 accumulator layout of one contraction is reused directly as the
 //     bf16 B operand of the next (P_bar V, dS K, P^T dO, dS^T Q): the k index
-//     of each MFMA is permuted to match, and the other operand is read from an
-//     LDS copy stored transposed;
-//   * K/V (forward, dQ pass) or Q/dO (dK/dV pass) tiles are staged through
-//     LDS, double-buffered, one barrier per tile;
-//   * causal work is ordered heaviest tile first.
+//     of each MFMA is permuted to match, and the other operand is read
+//     transposed out of the row-major LDS tile with ds_read_b64_tr_b16;
+//   * tiles go global -> LDS directly (global_load_lds_dwordx4, no staging
+//     registers) into an XOR-swizzled row-major layout, double-buffered, one
+//     barrier per tile; rows past N are clamped to row N-1 and masked;
+//   * all tiles of one (b, h) run on one XCD (its L2 keeps the head's
+//     operands) and causal work is ordered heaviest tile first.
 //
 // MFMA 32x32x16 lane layout (lane l, half h = l / 32):
 //   A (32 x 16): lane l holds row l % 32, k = 8h .. 8h+7
 //   B (16 x 32): lane l holds col l % 32, k = 8h .. 8h+7
 //   C (32 x 32): element r of lane l is row 8(r/4) + 4h + r%4, col l % 32
+// ds_read_b64_tr_b16: within each 16-lane group, lane L supplies an 8-byte
+//   address; lane l receives element l%4 of the reads of lanes (l%16)/4 + 4t,
+//   t = 0..3.  Reading a 4-row x 16-column block (lane L: row L/4, columns
+//   4(L%4)..+3) hands lane l column l%16 of those 4 rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,6 +47,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -59,8 +67,12 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_c
 
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor32f(float v) { return __shfl_xor(v, 32); }
-__device__ __forceinline__ int xor32i(int v) { return __shfl_xor(v, 32); }
+// Combine the two 32-lane halves (lane l and lane l ^ 32 hold the same row).
+__device__ __forceinline__ float max32(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+__device__ __forceinline__ float sum32(float v) { return v + __shfl_xor(v, 32); }
+__device__ __forceinline__ int sum32i(int v) { return v + __shfl_xor(v, 32); }
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // eight fp32 accumulator values -> the bf16 B operand of the next contraction
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
@@ -74,80 +86,68 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
   return r;
 }
 
-// A operand from a transposed LDS tile T[c][n] (pitch P elements): row c, the
-// 8 k slots of lane half h are n0 + 4h + {0..3} and n0 + 8 + 4h + {0..3}.
-__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* row_c, int n0, int h) {
-  u32x2 a = *reinterpret_cast<const u32x2*>(row_c + n0 + 4 * h);
-  u32x2 b = *reinterpret_cast<const u32x2*>(row_c + n0 + 8 + 4 * h);
-  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
-}
-
-// Stage rows [r0, r0+R) x D of a bf16 [N][D] matrix into LDS, row-major with
-// pitch P; rows >= N become zeros.
-template <int R, int D, int P>
-__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ src, int r0, int N, int tid,
-                                          u32x4 (&reg)[(R * D / 8 + 255) / 256]) {
-  constexpr int CH = D / 8, TOT = R * CH, PER = (TOT + 255) / 256;
-#pragma unroll
-  for (int c = 0; c < PER; ++c) {
-    const int idx = tid + c * 256;
-    const int row = idx / CH, ch = idx % CH;
-    const int r = r0 + row;
-    reg[c] = (idx < TOT && r < N) ? ld16(src + (size_t)r * D + ch * 8) : u32x4{0, 0, 0, 0};
+// ---------------------------------------------------------------------------
+// LDS tiles: R rows x D bf16, row-major, rows of D/8 16-byte chunks; chunk c
+// of row r sits at chunk c ^ (r & 7), so the eight rows a ds_read_b128 phase
+// touches land on distinct banks.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;
+  __device__ static __forceinline__ int chunk(int r, int c) { return r * CPR + (c ^ (r & 7)); }
+  // 8 bf16 of row r starting at column 8c (an MFMA A/B row operand)
+  __device__ static __forceinline__ bf16x8 row8(const uint16_t* t, int r, int c) {
+    return as_bf16x8(ld16(t + chunk(r, c) * 8));
   }
-}
-template <int R, int D, int P>
-__device__ __forceinline__ void store_rows(uint16_t* dst, int tid, const u32x4 (&reg)[(R * D / 8 + 255) / 256]) {
-  constexpr int CH = D / 8, TOT = R * CH, PER = (TOT + 255) / 256;
-#pragma unroll
-  for (int c = 0; c < PER; ++c) {
-    const int idx = tid + c * 256;
-    if (idx < TOT) {
-      const int row = idx / CH, ch = idx % CH;
-      *reinterpret_cast<u32x4*>(dst + row * P + ch * 8) = reg[c];
-    }
+  // transposed read: 4 bf16 of rows (the 16-lane block pattern) at column col (multiple of 4)
+  __device__ static __forceinline__ u32x2 tr4(const uint16_t* t, int r, int col) {
+    const uint16_t* p = t + chunk(r, col >> 3) * 8 + (col & 7);
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
   }
-}
-
-// Stage the same rows transposed: T[c][row] with pitch P (>= R, P % 4 == 0).
-// A task is 4 consecutive rows x 8 columns: four 16-byte loads, eight 8-byte
-// LDS stores.  Tasks are spread over the threads [t0, t0 + 256).
-template <int R, int D>
-struct TrTask {
-  static constexpr int CH = D / 8, TOT = (R / 4) * CH, PER = (TOT + 255) / 256;
+  // A operand of X^T (rows = columns of the tile, k = tile rows): for lane l,
+  // column 32*cb + l%32, tile rows r0 + 4h + {0..3} and r0 + 8 + 4h + {0..3}.
+  __device__ static __forceinline__ bf16x8 trans8(const uint16_t* t, int r0, int cb, int lane) {
+    const int L = lane & 15, h = lane >> 5, G = (lane >> 4) & 1;
+    const int r = r0 + 4 * h + (L >> 2);
+    const int col = 32 * cb + 16 * G + 4 * (L & 3);
+    const u32x2 a = tr4(t, r, col);
+    const u32x2 b = tr4(t, r + 8, col);
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+  }
 };
+
+// Rows [r0, r0+R) of a bf16 [N][D] matrix straight into a swizzled LDS tile;
+// every thread of the 256 issues (R*D/8)/256 16-byte loads.  Rows past N read
+// row N-1 (finite data; the kernels mask them).
 template <int R, int D>
-__device__ __forceinline__ void load_rows_tr(const uint16_t* __restrict__ src, int r0, int N, int tid,
-                                             u32x4 (&reg)[TrTask<R, D>::PER][4]) {
-  constexpr int CH = TrTask<R, D>::CH, TOT = TrTask<R, D>::TOT, PER = TrTask<R, D>::PER;
+__device__ __forceinline__ void tile_to_lds(const uint16_t* __restrict__ src, int r0, int N, uint16_t* tile,
+                                            int wu, int lane) {
+  constexpr int CPR = D / 8, TOT = R * CPR, PER = TOT / 256;
+  static_assert(TOT % 256 == 0, "tile must be a whole number of workgroup loads");
 #pragma unroll
-  for (int c = 0; c < PER; ++c) {
-    const int idx = tid + c * 256;
-    const int rg = idx / CH, ch = idx % CH;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = r0 + 4 * rg + q;
-      reg[c][q] = (idx < TOT && r < N) ? ld16(src + (size_t)r * D + ch * 8) : u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < PER; ++i) {
+    const int P = i * 256 + wu * 64 + lane;
+    const int r = P / CPR, p = P % CPR;
+    const int c = p ^ (r & 7);
+    int gr = r0 + r;
+    gr = gr < N ? gr : N - 1;
+    __builtin_amdgcn_global_load_lds(src + (size_t)gr * D + c * 8, (lds_void*)(tile + (i * 256 + wu * 64) * 8), 16,
+                                     0, 0);
   }
 }
-template <int R, int D, int P>
-__device__ __forceinline__ void store_rows_tr(uint16_t* dst, int tid, const u32x4 (&reg)[TrTask<R, D>::PER][4]) {
-  constexpr int CH = TrTask<R, D>::CH, TOT = TrTask<R, D>::TOT, PER = TrTask<R, D>::PER;
-#pragma unroll
-  for (int c = 0; c < PER; ++c) {
-    const int idx = tid + c * 256;
-    if (idx < TOT) {
-      const int rg = idx / CH, ch = idx % CH;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int p = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(reg[c][1][p], reg[c][0][p], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(reg[c][3][p], reg[c][2][p], sel);
-        *reinterpret_cast<u32x2*>(dst + (ch * 8 + e) * P + 4 * rg) = u32x2{lo, hi};
-      }
-    }
+
+// Workgroup L -> (tile rank, head).  Workgroups are dispatched to the 8 XCDs
+// round-robin (L % 8); with B*H a multiple of 8 every tile of head bh runs on
+// XCD bh % 8.  Rank 0 is dispatched first.
+__device__ __forceinline__ void map_block(int L, int BH, int& rank, int& bh) {
+  if ((BH & 7) == 0) {
+    const int xcd = L & 7, j = L >> 3, hpx = BH >> 3;
+    rank = j / hpx;
+    bh = (j % hpx) * 8 + xcd;
+  } else {
+    rank = L / BH;
+    bh = L % BH;
   }
 }
 
@@ -160,38 +160,58 @@ __device__ __forceinline__ float shifted(float m, int c, float base, int stabili
   return base;
 }
 
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, float c, float d) {
+  bf16x2 x = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  bf16x2 y = __builtin_convertvector(f32x2{c, d}, bf16x2);
+  *reinterpret_cast<u32x2*>(p) = u32x2{__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y)};
+}
+
 // ---------------------------------------------------------------------------
 // Forward (and, with TIES_ONLY, the duplicate-max detector alone).
 // One workgroup = 128 queries of one (b, h); 4 waves x 32 queries; KV tiles of
-// 64 keys.  Per tile and wave: S^T = K Q^T (D/16 x 2 MFMAs), the online
-// (max, count) merge and shift, P_bar = exp2(S t - m2), O^T += V^T P_bar^T.
+// BN keys.  Per tile and wave: S^T = K Q^T, the online (max, count) merge and
+// shift, P_bar = exp2(S t - m2), O^T += V^T P_bar^T.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool TIES_ONLY>
+template <int D, int BN, bool CAUSAL, bool TIES_ONLY>
+struct Fwd {
+  static constexpr int BM = 128, NKB = BN / 32, NKK = D / 16, NCB = D / 32;
+  static constexpr int TILE = BN * D;  // bf16 elements per K or V tile
+};
+
+template <int D, int BN, bool CAUSAL, bool TIES_ONLY>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int32_t* __restrict__ TIES,
     int32_t* __restrict__ PONE, int32_t* __restrict__ FORMED, float* __restrict__ ROWMAX, int BH, int N,
     float scale, int stabilise, float beta, int nqt) {
-  constexpr int BM = 128, BN = 64, KP = D + 8, VP = BN + 4, NKK = D / 16, NCB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[TIES_ONLY ? 1 : 2][TIES_ONLY ? 8 : D * VP];
+  using F = Fwd<D, BN, CAUSAL, TIES_ONLY>;
+  constexpr int BM = F::BM, NKB = F::NKB, NKK = F::NKK, NCB = F::NCB, TILE = F::TILE;
+  constexpr int NT = TIES_ONLY ? 1 : 2;  // K (and V) per buffer
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * NT * TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, h = lane >> 5;
-  const int L = blockIdx.x;
-  const int qt = CAUSAL ? (nqt - 1 - L / BH) : (L / BH);
-  const int bh = L % BH;
+  int rank, bh;
+  map_block(blockIdx.x, BH, rank, bh);
+  const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
   const size_t head = (size_t)bh * N * D;
-  const int q0 = qt * BM, qw = q0 + 32 * w, qi = qw + li;
+  const int q0 = qt * BM, qw = q0 + 32 * wu, qi = qw + li;
   const float t = scale * kLog2e;
+
+  const int kend = CAUSAL ? min(q0 + BM, N) : N;
+  const int nkt = (kend + BN - 1) / BN;
+  auto fetch = [&](int kt, int buf) {
+    uint16_t* base = lds + buf * NT * TILE;
+    tile_to_lds<BN, D>(K + head, kt * BN, N, base, wu, lane);
+    if constexpr (!TIES_ONLY) tile_to_lds<BN, D>(V + head, kt * BN, N, base + TILE, wu, lane);
+  };
+  fetch(0, 0);
 
   bf16x8 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
     qf[kk] = as_bf16x8(qi < N ? ld16(Q + head + (size_t)qi * D + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
-
-  const int kend = CAUSAL ? min(q0 + BM, N) : N;
-  const int nkt = (kend + BN - 1) / BN;
 
   f32x16 oacc[NCB];
 #pragma unroll
@@ -200,105 +220,85 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   int c_run = 0, ones = 0;
   const bool count_ones = FORMED != nullptr;
 
-  u32x4 kreg[(BN * D / 8 + 255) / 256];
-  u32x4 vreg[TrTask<BN, D>::PER][4];
-  auto fetch = [&](int kt) {
-    load_rows<BN, D, KP>(K + head, kt * BN, N, tid, kreg);
-    if constexpr (!TIES_ONLY) load_rows_tr<BN, D>(V + head, kt * BN, N, tid, vreg);
-  };
-  auto commit = [&](int buf) {
-    store_rows<BN, D, KP>(Ks[buf], tid, kreg);
-    if constexpr (!TIES_ONLY) store_rows_tr<BN, D, VP>(Vt[buf], tid, vreg);
-  };
-  fetch(0);
-  commit(0);
-  __syncthreads();
-
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nkt) fetch(kt + 1);
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < nkt) fetch(kt + 1, buf ^ 1);
+    const uint16_t* Kt = lds + buf * NT * TILE;
+    const uint16_t* Vt = Kt + TILE;
     const int k0 = kt * BN;
     const bool active = qw < N && (!CAUSAL || k0 <= qw + 31);
-    if (active) {
-      f32x16 s[2];
+    if (!active) continue;
+
+    f32x16 s[NKB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const uint16_t* kp = &Ks[buf][(32 * kb + li) * KP + 8 * h];
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) s[kb] = mfma(as_bf16x8(ld16(kp + 16 * kk)), qf[kk], s[kb]);
-      }
-      const bool need_mask = (CAUSAL && k0 + BN - 1 > qw) || (k0 + BN > N);
-      if (need_mask) {
+      for (int kk = 0; kk < NKK; ++kk) s[kb] = mfma(Tile<D>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
+    }
+    if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-            if ((CAUSAL && key > qi) || key >= N) s[kb][r] = -INFINITY;
-          }
-      }
-      // tile (max, count) on the raw fp32 dot products, then the running merge
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, xor32f(mx));
-      int cnt = 0;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cnt += (s[kb][r] == mx) ? 1 : 0;
-      cnt += xor32i(cnt);
-      if (mx == -INFINITY) cnt = 0;
-      if (mx > m_run) {
-        m_run = mx;
-        c_run = cnt;
-      } else if (mx == m_run) {
-        c_run += cnt;
-      }
-      if constexpr (!TIES_ONLY) {
-        const float base = m_run * t;
-        const float m2 = shifted(m_run, c_run, base, stabilise, beta);
-        const float alpha = (m2_run == -INFINITY) ? 0.f : exp2f_fast(m2_run - m2);
-        m2_run = m2;
-        lsum *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) oacc[cb] *= alpha;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = exp2f_fast(__builtin_fmaf(s[kb][r], t, -m2));
-            s[kb][r] = p;
-            lsum += p;
-          }
-        if (count_ones) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ones += (s[kb][r] >= kBf16OneLow) ? 1 : 0;
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if ((CAUSAL && key > qi) || key >= N) s[kb][r] = -INFINITY;
         }
-        bf16x8 pb[2][2];
+    }
+    // tile (max, count) on the raw fp32 dot products, then the running merge
+    float mx = s[0][0];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          pb[kb][0] = pack8(s[kb], 0);
-          pb[kb][1] = pack8(s[kb], 8);
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max32(mx);
+    int cnt = 0;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cnt += (s[kb][r] == mx) ? 1 : 0;
+    cnt = sum32i(cnt);
+    if (mx == -INFINITY) cnt = 0;
+    if (mx > m_run) {
+      m_run = mx;
+      c_run = cnt;
+    } else if (mx == m_run) {
+      c_run += cnt;
+    }
+    if constexpr (!TIES_ONLY) {
+      const float base = m_run * t;
+      const float m2 = shifted(m_run, c_run, base, stabilise, beta);
+      const float alpha = (m2_run == -INFINITY) ? 0.f : exp2f_fast(m2_run - m2);
+      m2_run = m2;
+      lsum *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) oacc[cb] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2f_fast(__builtin_fmaf(s[kb][r], t, -m2));
+          s[kb][r] = p;
+          lsum += p;
         }
+      if (count_ones) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ones += (s[kb][r] >= kBf16OneLow) ? 1 : 0;
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 p0 = pack8(s[kb], 0), p1 = pack8(s[kb], 8);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          const uint16_t* vp = &Vt[buf][(32 * cb + li) * VP];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-              oacc[cb] = mfma(lds_tr_operand(vp, 32 * kb + 16 * m, h), pb[kb][m], oacc[cb]);
+          oacc[cb] = mfma(Tile<D>::trans8(Vt, 32 * kb, cb, lane), p0, oacc[cb]);
+          oacc[cb] = mfma(Tile<D>::trans8(Vt, 32 * kb + 16, cb, lane), p1, oacc[cb]);
         }
       }
     }
-    if (kt + 1 < nkt) commit(buf ^ 1);
-    __syncthreads();
   }
 
   if (qw >= N) return;
@@ -309,20 +309,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
       if (ROWMAX) ROWMAX[row] = scale * m_run;
     }
   } else {
-    const float ltot = lsum + xor32f(lsum);
-    const int ones_tot = ones + xor32i(ones);
+    const float ltot = sum32(lsum);
+    const int ones_tot = sum32i(ones);
     const float inv = 1.0f / ltot;
     if (qi < N) {
       uint16_t* op = O + head + (size_t)qi * D;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x2 a = __builtin_convertvector(f32x2{oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv}, bf16x2);
-          bf16x2 b = __builtin_convertvector(f32x2{oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv}, bf16x2);
-          *reinterpret_cast<u32x2*>(op + 32 * cb + 8 * g + 4 * h) =
-              u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
-        }
+        for (int g = 0; g < 4; ++g)
+          store_bf16x4(op + 32 * cb + 8 * g + 4 * h, oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv,
+                       oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
       if (h == 0) {
         LSE[row] = (m2_run + __builtin_amdgcn_logf(ltot)) * kLn2;
         if (TIES) TIES[row] = c_run;
@@ -341,25 +338,32 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 // S^T = K Q^T, P = exp2(S t - lse2), dP^T = V dO^T, dS = P (dP - delta),
 // dQ^T += K^T dS^T.  One workgroup = 128 queries; KV tiles of BN keys.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ Og, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
     uint16_t* __restrict__ dQ, float* __restrict__ DELTA, int BH, int N, float scale, int nqt) {
-  constexpr int BM = 128, BN = (D == 64 ? 64 : 32), NKB = BN / 32, KP = D + 8, TP = BN + 4;
-  constexpr int NKK = D / 16, NCB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * TP];
+  constexpr int BM = 128, NKB = BN / 32, NKK = D / 16, NCB = D / 32, TILE = BN * D;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, h = lane >> 5;
-  const int L = blockIdx.x;
-  const int qt = CAUSAL ? (nqt - 1 - L / BH) : (L / BH);
-  const int bh = L % BH;
+  int rank, bh;
+  map_block(blockIdx.x, BH, rank, bh);
+  const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
   const size_t head = (size_t)bh * N * D;
-  const int q0 = qt * BM, qw = q0 + 32 * w, qi = qw + li;
+  const int q0 = qt * BM, qw = q0 + 32 * wu, qi = qw + li;
   const float t = scale * kLog2e;
+
+  const int kend = CAUSAL ? min(q0 + BM, N) : N;
+  const int nkt = (kend + BN - 1) / BN;
+  auto fetch = [&](int kt, int buf) {
+    uint16_t* base = lds + buf * 2 * TILE;
+    tile_to_lds<BN, D>(K + head, kt * BN, N, base, wu, lane);
+    tile_to_lds<BN, D>(V + head, kt * BN, N, base + TILE, wu, lane);
+  };
+  fetch(0, 0);
 
   bf16x8 qf[NKK], gf[NKK];
   float dl = 0.f;
@@ -373,81 +377,61 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) dl += (float)gf[kk][e] * (float)of[e];
   }
-  dl += xor32f(dl);
+  dl = sum32(dl);
   const float lse2 = qi < N ? LSE[(size_t)bh * N + qi] * kLog2e : 0.f;
   if (h == 0 && qi < N) DELTA[(size_t)bh * N + qi] = dl;
 
-  const int kend = CAUSAL ? min(q0 + BM, N) : N;
-  const int nkt = (kend + BN - 1) / BN;
   f32x16 dqa[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) dqa[cb] = f32x16{};
 
-  u32x4 kreg[(BN * D / 8 + 255) / 256], vreg[(BN * D / 8 + 255) / 256];
-  u32x4 treg[TrTask<BN, D>::PER][4];
-  auto fetch = [&](int kt) {
-    load_rows<BN, D, KP>(K + head, kt * BN, N, tid, kreg);
-    load_rows<BN, D, KP>(V + head, kt * BN, N, tid, vreg);
-    load_rows_tr<BN, D>(K + head, kt * BN, N, tid, treg);
-  };
-  auto commit = [&](int buf) {
-    store_rows<BN, D, KP>(Ks[buf], tid, kreg);
-    store_rows<BN, D, KP>(Vs[buf], tid, vreg);
-    store_rows_tr<BN, D, TP>(Kt[buf], tid, treg);
-  };
-  fetch(0);
-  commit(0);
-  __syncthreads();
-
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nkt) fetch(kt + 1);
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < nkt) fetch(kt + 1, buf ^ 1);
+    const uint16_t* Kt = lds + buf * 2 * TILE;
+    const uint16_t* Vt = Kt + TILE;
     const int k0 = kt * BN;
     const bool active = qw < N && (!CAUSAL || k0 <= qw + 31);
-    if (active) {
-      f32x16 s[NKB], dp[NKB];
+    if (!active) continue;
+
+    f32x16 s[NKB], dp[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
-        const uint16_t* kp = &Ks[buf][(32 * kb + li) * KP + 8 * h];
-        const uint16_t* vp = &Vs[buf][(32 * kb + li) * KP + 8 * h];
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          s[kb] = mfma(as_bf16x8(ld16(kp + 16 * kk)), qf[kk], s[kb]);
-          dp[kb] = mfma(as_bf16x8(ld16(vp + 16 * kk)), gf[kk], dp[kb]);
-        }
+      for (int kk = 0; kk < NKK; ++kk) {
+        s[kb] = mfma(Tile<D>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
+        dp[kb] = mfma(Tile<D>::row8(Vt, 32 * kb + li, 2 * kk + h), gf[kk], dp[kb]);
       }
-      const bool need_mask = (CAUSAL && k0 + BN - 1 > qw) || (k0 + BN > N);
+    }
+    if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r];
-          if (need_mask) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-            if ((CAUSAL && key > qi) || key >= N) x = -INFINITY;
-          }
-          const float p = exp2f_fast(__builtin_fmaf(x, t, -lse2));
-          s[kb][r] = p * (dp[kb][r] - dl);
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if ((CAUSAL && key > qi) || key >= N) s[kb][r] = -INFINITY;
         }
-      bf16x8 db[NKB][2];
+    }
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        db[kb][0] = pack8(s[kb], 0);
-        db[kb][1] = pack8(s[kb], 8);
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f_fast(__builtin_fmaf(s[kb][r], t, -lse2));
+        s[kb][r] = p * (dp[kb][r] - dl);
       }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const bf16x8 d0 = pack8(s[kb], 0), d1 = pack8(s[kb], 8);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const uint16_t* tp = &Kt[buf][(32 * cb + li) * TP];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int m = 0; m < 2; ++m) dqa[cb] = mfma(lds_tr_operand(tp, 32 * kb + 16 * m, h), db[kb][m], dqa[cb]);
+        dqa[cb] = mfma(Tile<D>::trans8(Kt, 32 * kb, cb, lane), d0, dqa[cb]);
+        dqa[cb] = mfma(Tile<D>::trans8(Kt, 32 * kb + 16, cb, lane), d1, dqa[cb]);
       }
     }
-    if (kt + 1 < nkt) commit(buf ^ 1);
-    __syncthreads();
   }
 
   if (qi >= N) return;
@@ -455,12 +439,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x2 a = __builtin_convertvector(f32x2{dqa[cb][4 * g] * scale, dqa[cb][4 * g + 1] * scale}, bf16x2);
-      bf16x2 b = __builtin_convertvector(f32x2{dqa[cb][4 * g + 2] * scale, dqa[cb][4 * g + 3] * scale}, bf16x2);
-      *reinterpret_cast<u32x2*>(qp + 32 * cb + 8 * g + 4 * h) =
-          u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
-    }
+    for (int g = 0; g < 4; ++g)
+      store_bf16x4(qp + 32 * cb + 8 * g + 4 * h, dqa[cb][4 * g] * scale, dqa[cb][4 * g + 1] * scale,
+                   dqa[cb][4 * g + 2] * scale, dqa[cb][4 * g + 3] * scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -468,28 +449,47 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 // BQ rows.  Per tile: S = Q K^T (keys on the lane axis), P = exp2(S t - lse2),
 // dP = dO V^T, dS = P (dP - delta), dV^T += dO^T P, dK^T += Q^T dS.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+template <int D, int BQ, bool CAUSAL>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale) {
-  constexpr int BK = 128, BQ = (D == 64 ? 64 : 32), NQB = BQ / 32, KP = D + 8, TP = BQ + 4;
-  constexpr int NKK = D / 16, NCB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Gs[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TP];
-  __shared__ __attribute__((aligned(16))) uint16_t Gt[2][D * TP];
-  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale, int nkt) {
+  constexpr int BK = 128, NQB = BQ / 32, NKK = D / 16, NCB = D / 32, TILE = BQ * D;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][BQ];  // [buf][lse2, delta][row]
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, h = lane >> 5;
-  const int L = blockIdx.x;
-  const int kt = L / BH;   // causal: the first key tiles see the most queries
-  const int bh = L % BH;
+  int rank, bh;
+  map_block(blockIdx.x, BH, rank, bh);
+  const int kt = rank;  // causal: the first key tiles see the most queries
   const size_t head = (size_t)bh * N * D;
-  const int k0 = kt * BK, kw = k0 + 32 * w, kj = kw + li;
+  const size_t hrow = (size_t)bh * N;
+  const int k0 = kt * BK, kw = k0 + 32 * wu, kj = kw + li;
   const float t = scale * kLog2e;
+
+  const int qstart = CAUSAL ? (k0 / BQ) : 0;
+  const int nqt = (N + BQ - 1) / BQ;
+  float rl = 0.f, rd = 0.f;
+  auto fetch = [&](int qt, int buf) {
+    uint16_t* base = lds + buf * 2 * TILE;
+    tile_to_lds<BQ, D>(Q + head, qt * BQ, N, base, wu, lane);
+    tile_to_lds<BQ, D>(dO + head, qt * BQ, N, base + TILE, wu, lane);
+    if (tid < BQ) {
+      int r = qt * BQ + tid;
+      r = r < N ? r : N - 1;
+      rl = LSE[hrow + r] * kLog2e;
+      rd = DELTA[hrow + r];
+    }
+  };
+  auto commit_rows = [&](int buf) {
+    if (tid < BQ) {
+      rowv[buf][0][tid] = rl;
+      rowv[buf][1][tid] = rd;
+    }
+  };
+  fetch(qstart, 0);
 
   bf16x8 kf[NKK], vf[NKK];
 #pragma unroll
@@ -505,44 +505,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     dka[cb] = f32x16{};
     dva[cb] = f32x16{};
   }
+  wait_vmem();
+  commit_rows(0);
 
-  const int qstart = CAUSAL ? (k0 / BQ) : 0;
-  const int nqt = (N + BQ - 1) / BQ;
-
-  u32x4 qreg[(BQ * D / 8 + 255) / 256], greg[(BQ * D / 8 + 255) / 256];
-  u32x4 qtr[TrTask<BQ, D>::PER][4], gtr[TrTask<BQ, D>::PER][4];
-  float lreg = 0.f, dreg = 0.f;
-  auto fetch = [&](int qt) {
-    const int r0 = qt * BQ;
-    load_rows<BQ, D, KP>(Q + head, r0, N, tid, qreg);
-    load_rows<BQ, D, KP>(dO + head, r0, N, tid, greg);
-    load_rows_tr<BQ, D>(Q + head, r0, N, tid, qtr);
-    load_rows_tr<BQ, D>(dO + head, r0, N, tid, gtr);
-    if (tid < BQ) {
-      const int r = r0 + tid;
-      lreg = r < N ? LSE[(size_t)bh * N + r] * kLog2e : INFINITY;   // rows past N: P = 0
-      dreg = r < N ? DELTA[(size_t)bh * N + r] : 0.f;
-    }
-  };
-  auto commit = [&](int buf) {
-    store_rows<BQ, D, KP>(Qs[buf], tid, qreg);
-    store_rows<BQ, D, KP>(Gs[buf], tid, greg);
-    store_rows_tr<BQ, D, TP>(Qt[buf], tid, qtr);
-    store_rows_tr<BQ, D, TP>(Gt[buf], tid, gtr);
-    if (tid < BQ) {
-      Ls[buf][tid] = lreg;
-      Ds[buf][tid] = dreg;
-    }
-  };
-  if (qstart < nqt && k0 < N) {
-    fetch(qstart);
-    commit(0);
-  }
-  __syncthreads();
-
-  for (int qt = qstart; qt < nqt && k0 < N; ++qt) {
+  for (int qt = qstart; qt < nqt; ++qt) {
     const int buf = (qt - qstart) & 1;
-    if (qt + 1 < nqt) fetch(qt + 1);
+    wait_vmem();
+    __syncthreads();
+    if (qt + 1 < nqt) fetch(qt + 1, buf ^ 1);
+    const uint16_t* Qt = lds + buf * 2 * TILE;
+    const uint16_t* Gt = Qt + TILE;
     const int r0 = qt * BQ;
     const bool active = kw < N && (!CAUSAL || r0 + BQ - 1 >= kw);
     if (active) {
@@ -551,53 +523,53 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int qb = 0; qb < NQB; ++qb) {
         s[qb] = f32x16{};
         dp[qb] = f32x16{};
-        const uint16_t* qp = &Qs[buf][(32 * qb + li) * KP + 8 * h];
-        const uint16_t* gp = &Gs[buf][(32 * qb + li) * KP + 8 * h];
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          s[qb] = mfma(as_bf16x8(ld16(qp + 16 * kk)), kf[kk], s[qb]);
-          dp[qb] = mfma(as_bf16x8(ld16(gp + 16 * kk)), vf[kk], dp[qb]);
+          s[qb] = mfma(Tile<D>::row8(Qt, 32 * qb + li, 2 * kk + h), kf[kk], s[qb]);
+          dp[qb] = mfma(Tile<D>::row8(Gt, 32 * qb + li, 2 * kk + h), vf[kk], dp[qb]);
         }
       }
-      const bool need_mask = CAUSAL && r0 < kw + 31;
-      bf16x8 pb[NQB][2], db[NQB][2];
+      if ((CAUSAL && r0 < kw + 31) || r0 + BQ > N) {
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qrow = r0 + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
+            if ((CAUSAL && qrow < kj) || qrow >= N) s[qb][r] = -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int rl = 32 * qb + 8 * g + 4 * h;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][rl]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][rl]);
+          const int rr = 32 * qb + 8 * g + 4 * h;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&rowv[buf][0][rr]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&rowv[buf][1][rr]);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int r = 4 * g + jj;
-            float x = s[qb][r];
-            if (need_mask && r0 + rl + jj < kj) x = -INFINITY;
-            const float p = exp2f_fast(__builtin_fmaf(x, t, -l4[jj]));
+            const float p = exp2f_fast(__builtin_fmaf(s[qb][r], t, -l4[jj]));
             s[qb][r] = p;
             dp[qb][r] = p * (dp[qb][r] - d4[jj]);
           }
         }
-        pb[qb][0] = pack8(s[qb], 0);
-        pb[qb][1] = pack8(s[qb], 8);
-        db[qb][0] = pack8(dp[qb], 0);
-        db[qb][1] = pack8(dp[qb], 8);
-      }
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const uint16_t* gt = &Gt[buf][(32 * cb + li) * TP];
-        const uint16_t* qtp = &Qt[buf][(32 * cb + li) * TP];
+      for (int qb = 0; qb < NQB; ++qb) {
+        const bf16x8 p0 = pack8(s[qb], 0), p1 = pack8(s[qb], 8);
+        const bf16x8 d0 = pack8(dp[qb], 0), d1 = pack8(dp[qb], 8);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            dva[cb] = mfma(lds_tr_operand(gt, 32 * qb + 16 * m, h), pb[qb][m], dva[cb]);
-            dka[cb] = mfma(lds_tr_operand(qtp, 32 * qb + 16 * m, h), db[qb][m], dka[cb]);
-          }
+        for (int cb = 0; cb < NCB; ++cb) {
+          dva[cb] = mfma(Tile<D>::trans8(Gt, 32 * qb, cb, lane), p0, dva[cb]);
+          dva[cb] = mfma(Tile<D>::trans8(Gt, 32 * qb + 16, cb, lane), p1, dva[cb]);
+          dka[cb] = mfma(Tile<D>::trans8(Qt, 32 * qb, cb, lane), d0, dka[cb]);
+          dka[cb] = mfma(Tile<D>::trans8(Qt, 32 * qb + 16, cb, lane), d1, dka[cb]);
+        }
       }
     }
-    if (qt + 1 < nqt) commit(buf ^ 1);
-    __syncthreads();
+    if (qt + 1 < nqt) {
+      wait_vmem();
+      commit_rows(buf ^ 1);
+    }
   }
 
   if (kj >= N) return;
@@ -607,25 +579,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      bf16x2 a = __builtin_convertvector(f32x2{dka[cb][4 * g] * scale, dka[cb][4 * g + 1] * scale}, bf16x2);
-      bf16x2 b = __builtin_convertvector(f32x2{dka[cb][4 * g + 2] * scale, dka[cb][4 * g + 3] * scale}, bf16x2);
-      *reinterpret_cast<u32x2*>(kp + 32 * cb + 8 * g + 4 * h) =
-          u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
-      bf16x2 c = __builtin_convertvector(f32x2{dva[cb][4 * g], dva[cb][4 * g + 1]}, bf16x2);
-      bf16x2 d = __builtin_convertvector(f32x2{dva[cb][4 * g + 2], dva[cb][4 * g + 3]}, bf16x2);
-      *reinterpret_cast<u32x2*>(vp + 32 * cb + 8 * g + 4 * h) =
-          u32x2{__builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+      store_bf16x4(kp + 32 * cb + 8 * g + 4 * h, dka[cb][4 * g] * scale, dka[cb][4 * g + 1] * scale,
+                   dka[cb][4 * g + 2] * scale, dka[cb][4 * g + 3] * scale);
+      store_bf16x4(vp + 32 * cb + 8 * g + 4 * h, dva[cb][4 * g], dva[cb][4 * g + 1], dva[cb][4 * g + 2],
+                   dva[cb][4 * g + 3]);
     }
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+constexpr int kFwdBN = 64;
+
 template <int D, bool CAUSAL, bool TIES_ONLY>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int nqt = (a.N + 127) / 128;
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, TIES_ONLY>), dim3(nqt * BH), dim3(256), 0, st,
+  hipLaunchKernelGGL((fwd_kernel<D, kFwdBN, CAUSAL, TIES_ONLY>), dim3(nqt * BH), dim3(256), 0, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      a.ties, a.pbar_one, a.formed_ones, a.rowmax, BH, a.N, a.scale, a.stabilise, a.beta, nqt);
   return hipGetLastError();
@@ -642,9 +612,10 @@ hipError_t launch_tiecount(const FwdArgs& a, hipStream_t st) { return launch_fwd
 
 template <int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
+  constexpr int BN = 64;
   const int nqt = (a.N + 127) / 128;
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(nqt * BH), dim3(256), 0, st, (const uint16_t*)a.q,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL>), dim3(nqt * BH), dim3(256), 0, st, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o, (const uint16_t*)a.dO,
                      a.lse, (uint16_t*)a.dq, a.delta, BH, a.N, a.scale, nqt);
   return hipGetLastError();
@@ -652,11 +623,12 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
+  constexpr int BQ = (D == 64 ? 64 : 32);
   const int nkt = (a.N + 127) / 128;
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nkt * BH), dim3(256), 0, st, (const uint16_t*)a.q,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, CAUSAL>), dim3(nkt * BH), dim3(256), 0, st, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.delta,
-                     (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.N, a.scale);
+                     (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.N, a.scale, nkt);
   return hipGetLastError();
 }
 

@@ -1,0 +1,83 @@
+"""Signed-bias statistics of a bf16 kernel's outputs against the FP64 oracle.
+
+TEST INFRASTRUCTURE (part of the oracle package): used by tests/ and by the
+cpu_baseline leg of bench.py, on rows the oracle has computed.
+
+The pages' claim (itsolotime.com/archives/23922, section "机制解释二"): with
+repeated maxima, P_bar holds exact 1s, and where V is mostly negative the bf16
+accumulation of P_bar V drifts negative, so O_lp sits below O_hp; with dO also
+negative the error entering the backward through delta = rowsum(dO o O) is
+positive.  The statistic: on rows whose maximum repeats (rs >= 2) and on the
+negatively skewed V dimensions, the mean signed error of O in bf16 ulps of the
+reference, and of delta in units of u * sum_c |dO_ic O_ic| (u = 2^-8), with a
+row-clustered standard error (each row's mean is one sample) and z = mean/SEM.
+Controls: rows without a repeat, and the other dimensions.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+U_BF16 = 2.0 ** -8
+
+
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Spacing of the bf16 grid at |x| (normal range)."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7.0)
+
+
+def _stats(per_row: np.ndarray) -> dict:
+    per_row = per_row[np.isfinite(per_row)]
+    n = int(per_row.size)
+    if n == 0:
+        return {"n_rows": 0, "mean": None, "sem": None, "z": None}
+    mean = float(per_row.mean())
+    sem = float(per_row.std(ddof=1) / math.sqrt(n)) if n > 1 else float("nan")
+    z = mean / sem if sem and sem > 0 else float("nan")
+    return {"n_rows": n, "mean": mean, "sem": sem, "z": z}
+
+
+def o_bias(O_gpu, O_ref, rows_mask, dims) -> dict:
+    """Mean signed error of O (in bf16 ulps of the reference) over rows x dims."""
+    e = (O_gpu[..., dims] - O_ref[..., dims]) / ulp_bf16(O_ref[..., dims])
+    per_row = e.mean(axis=-1)[rows_mask]
+    out = _stats(per_row)
+    raw = (O_gpu[..., dims] - O_ref[..., dims]).mean(axis=-1)[rows_mask]
+    out["mean_abs_units"] = float(raw.mean()) if raw.size else None
+    return out
+
+
+def delta_bias(delta_gpu, delta_ref, dO, O_ref, rows_mask) -> dict:
+    """Mean signed error of delta in units of u * sum_c |dO_ic O_ic|."""
+    scale = U_BF16 * np.sum(np.abs(dO * O_ref), axis=-1)
+    e = (delta_gpu - delta_ref) / np.maximum(scale, 1e-300)
+    out = _stats(e[rows_mask])
+    raw = (delta_gpu - delta_ref)[rows_mask]
+    out["mean_abs_units"] = float(raw.mean()) if raw.size else None
+    return out
+
+
+def mode_difference(a: dict, b: dict) -> float:
+    """z of the difference of two means with independent standard errors."""
+    if not a.get("n_rows") or not b.get("n_rows") or a["sem"] is None or b["sem"] is None:
+        return float("nan")
+    den = math.sqrt(a["sem"] ** 2 + b["sem"] ** 2)
+    return (a["mean"] - b["mean"]) / den if den > 0 else float("nan")
+
+
+def report(O_gpu, O_ref, delta_gpu, delta_ref, dO, ties, rows_mask, skew_dims: int) -> dict:
+    """Bias of O and delta on tie rows x skewed dims, with the two controls."""
+    D = O_ref.shape[-1]
+    skew = np.arange(skew_dims)
+    rest = np.arange(skew_dims, D)
+    tie = rows_mask & (ties >= 2)
+    notie = rows_mask & (ties == 1)
+    return {
+        "O_tie_rows_skewed_dims": o_bias(O_gpu, O_ref, tie, skew),
+        "O_tie_rows_other_dims": o_bias(O_gpu, O_ref, tie, rest) if rest.size else None,
+        "O_single_max_rows_skewed_dims": o_bias(O_gpu, O_ref, notie, skew),
+        "delta_tie_rows": delta_bias(delta_gpu, delta_ref, dO, O_ref, tie),
+        "delta_single_max_rows": delta_bias(delta_gpu, delta_ref, dO, O_ref, notie),
+    }
