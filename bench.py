@@ -41,7 +41,22 @@ def parse():
     p.add_argument("--workload", default="gpt2_small")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the host oracle leg (profiling runs)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """One plain device-to-device copy of 1 GiB: reads 2^30 bytes, writes 2^30
+    bytes.  Profiled with the same FETCH_SIZE / WRITE_SIZE counters as the
+    attention kernels, it gives the factor from counter units to bytes."""
+    import torch
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}), flush=True)
 
 
 def kernel_hash() -> str:
@@ -63,6 +78,9 @@ def measured_traffic(kernel: str):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(attention heads shard across GPUs with no exchange; see the design notes). "
@@ -234,16 +252,18 @@ def cpu_leg(w, d, nss, t, stream):
         torch.cuda.synchronize()
         O = f["o"].float().cpu().numpy().astype(np.float64)
         dl = b["delta"].cpu().numpy().astype(np.float64)
+        O_round = inputs_f64(oracle.bf16_from_double(ref["O"], "rne"))
         rep = bias.report(O, ref["O"], dl, rb["delta"], gO, ref["ties"],
-                          np.ones(ref["ties"].shape, dtype=bool), w.v_skew_dims)
+                          np.ones(ref["ties"].shape, dtype=bool), w.v_skew_dims, O_ref_rounded=O_round)
         rep["max_err_over_tol"] = {
             "O": float(np.max(np.abs(O - ref["O"]) / ref["tol_O"])),
             "delta": float(np.max(np.abs(dl - rb["delta"]) / rb["tol_delta"]))}
         rep["pbar_one_events_on_tie_rows"] = int(f["pbar_one"].cpu().numpy()[ref["ties"] > 1].sum())
         rep["formed_ones_on_tie_rows"] = int(f["formed_ones"].cpu().numpy()[ref["ties"] > 1].sum())
         res["stabilised" if stabilise else "unstabilised"] = rep
-    res["O_mode_difference_z"] = bias.mode_difference(res["stabilised"]["O_tie_rows_skewed_dims"],
-                                                      res["unstabilised"]["O_tie_rows_skewed_dims"])
+    res["O_mode_difference_z"] = bias.mode_difference(
+        res["stabilised"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"],
+        res["unstabilised"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"])
     res["tie_rows"] = int((ref["ties"] > 1).sum())
     return cpu, res
 

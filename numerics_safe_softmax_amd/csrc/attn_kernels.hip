@@ -38,6 +38,10 @@
 
 #include "attn_launch.h"
 
+#ifndef NSS_FWD_STAGES
+#define NSS_FWD_STAGES 2
+#endif
+
 namespace nss {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -73,6 +77,12 @@ __device__ __forceinline__ float sum32(float v) { return v + __shfl_xor(v, 32); 
 __device__ __forceinline__ int sum32i(int v) { return v + __shfl_xor(v, 32); }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // eight fp32 accumulator values -> the bf16 B operand of the next contraction
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
@@ -186,8 +196,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     float scale, int stabilise, float beta, int nqt) {
   using F = Fwd<D, BN, CAUSAL, TIES_ONLY>;
   constexpr int BM = F::BM, NKB = F::NKB, NKK = F::NKK, NCB = F::NCB, TILE = F::TILE;
-  constexpr int NT = TIES_ONLY ? 1 : 2;  // K (and V) per buffer
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * NT * TILE];
+  constexpr int NT = TIES_ONLY ? 1 : 2;  // K (and V) per stage
+  constexpr int NS = NSS_FWD_STAGES;      // LDS stages: tiles in flight = NS - 1
+  constexpr int LOADS = NT * (TILE / 8 / 256);  // 16-byte loads per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NS * NT * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -206,12 +218,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     tile_to_lds<BN, D>(K + head, kt * BN, N, base, wu, lane);
     if constexpr (!TIES_ONLY) tile_to_lds<BN, D>(V + head, kt * BN, N, base + TILE, wu, lane);
   };
-  fetch(0, 0);
-
   bf16x8 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
     qf[kk] = as_bf16x8(qi < N ? ld16(Q + head + (size_t)qi * D + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
+  wait_vmem();
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nkt) fetch(st, st);
 
   f32x16 oacc[NCB];
 #pragma unroll
@@ -221,22 +235,40 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   const bool count_ones = FORMED != nullptr;
 
   for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    wait_vmem();
+    const int buf = kt % NS;
+    // tile kt has landed once only the later tiles' loads are outstanding
+    if (kt + NS - 2 < nkt) wait_vmem_le<LOADS * (NS - 2)>();
+    else wait_vmem();
     __syncthreads();
-    if (kt + 1 < nkt) fetch(kt + 1, buf ^ 1);
+    if (kt + NS - 1 < nkt) fetch(kt + NS - 1, (kt + NS - 1) % NS);
     const uint16_t* Kt = lds + buf * NT * TILE;
     const uint16_t* Vt = Kt + TILE;
     const int k0 = kt * BN;
     const bool active = qw < N && (!CAUSAL || k0 <= qw + 31);
     if (!active) continue;
 
+    // every LDS operand of the tile is requested up front: the K rows feed the
+    // score MFMAs, the transposed V reads complete under the softmax VALU work
+    bf16x8 ka[NKB][NKK];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = Tile<D>::row8(Kt, 32 * kb + li, 2 * kk + h);
     f32x16 s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s[kb] = mfma(Tile<D>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma(ka[kb][kk], qf[kk], s[kb]);
+    bf16x8 va[TIES_ONLY ? 1 : NKB][2][NCB];
+    if constexpr (!TIES_ONLY) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) va[kb][m][cb] = Tile<D>::trans8(Vt, 32 * kb + 16 * m, cb, lane);
     }
     if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
 #pragma unroll
@@ -294,8 +326,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
         const bf16x8 p0 = pack8(s[kb], 0), p1 = pack8(s[kb], 8);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          oacc[cb] = mfma(Tile<D>::trans8(Vt, 32 * kb, cb, lane), p0, oacc[cb]);
-          oacc[cb] = mfma(Tile<D>::trans8(Vt, 32 * kb + 16, cb, lane), p1, oacc[cb]);
+          oacc[cb] = mfma(va[kb][0][cb], p0, oacc[cb]);
+          oacc[cb] = mfma(va[kb][1][cb], p1, oacc[cb]);
         }
       }
     }
@@ -589,7 +621,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-constexpr int kFwdBN = 64;
+#ifndef NSS_FWD_BN
+#define NSS_FWD_BN 64
+#endif
+constexpr int kFwdBN = NSS_FWD_BN;  // keys per forward KV tile (64 or 128)
 
 template <int D, bool CAUSAL, bool TIES_ONLY>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {

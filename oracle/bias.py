@@ -39,12 +39,21 @@ def _stats(per_row: np.ndarray) -> dict:
     return {"n_rows": n, "mean": mean, "sem": sem, "z": z}
 
 
-def o_bias(O_gpu, O_ref, rows_mask, dims) -> dict:
-    """Mean signed error of O (in bf16 ulps of the reference) over rows x dims."""
-    e = (O_gpu[..., dims] - O_ref[..., dims]) / ulp_bf16(O_ref[..., dims])
+def o_bias(O_gpu, O_ref, rows_mask, dims, O_ref_rounded=None) -> dict:
+    """Mean signed error of O (in bf16 ulps of the reference) over rows x dims.
+
+    Against the exact reference the statistic also carries the bias that any
+    bf16 output has once the reference's values cluster at a power of two
+    (the grid spacing doubles there, so rounding errors measured in ulps of
+    the reference are not symmetric); against the correctly rounded reference
+    (``O_ref_rounded``, bf16 round-to-nearest-even of the exact value) that
+    part cancels and what remains is the bias of the computation itself.
+    """
+    ref = O_ref if O_ref_rounded is None else O_ref_rounded
+    e = (O_gpu[..., dims] - ref[..., dims]) / ulp_bf16(O_ref[..., dims])
     per_row = e.mean(axis=-1)[rows_mask]
     out = _stats(per_row)
-    raw = (O_gpu[..., dims] - O_ref[..., dims]).mean(axis=-1)[rows_mask]
+    raw = (O_gpu[..., dims] - ref[..., dims]).mean(axis=-1)[rows_mask]
     out["mean_abs_units"] = float(raw.mean()) if raw.size else None
     return out
 
@@ -67,17 +76,32 @@ def mode_difference(a: dict, b: dict) -> float:
     return (a["mean"] - b["mean"]) / den if den > 0 else float("nan")
 
 
-def report(O_gpu, O_ref, delta_gpu, delta_ref, dO, ties, rows_mask, skew_dims: int) -> dict:
-    """Bias of O and delta on tie rows x skewed dims, with the two controls."""
+def report(O_gpu, O_ref, delta_gpu, delta_ref, dO, ties, rows_mask, skew_dims: int,
+           O_ref_rounded=None) -> dict:
+    """Bias of O and delta on tie rows x skewed dims, with the two controls.
+
+    With ``O_ref_rounded`` given, the O statistics are also reported against
+    the correctly rounded reference, and delta against sum_c dO_ic * that
+    rounded O (what an exactly rounded bf16 forward would hand the backward).
+    """
     D = O_ref.shape[-1]
     skew = np.arange(skew_dims)
     rest = np.arange(skew_dims, D)
     tie = rows_mask & (ties >= 2)
     notie = rows_mask & (ties == 1)
-    return {
+    out = {
         "O_tie_rows_skewed_dims": o_bias(O_gpu, O_ref, tie, skew),
         "O_tie_rows_other_dims": o_bias(O_gpu, O_ref, tie, rest) if rest.size else None,
         "O_single_max_rows_skewed_dims": o_bias(O_gpu, O_ref, notie, skew),
         "delta_tie_rows": delta_bias(delta_gpu, delta_ref, dO, O_ref, tie),
         "delta_single_max_rows": delta_bias(delta_gpu, delta_ref, dO, O_ref, notie),
     }
+    if O_ref_rounded is not None:
+        d_round = np.sum(dO * O_ref_rounded, axis=-1)
+        out["vs_rounded_reference"] = {
+            "O_tie_rows_skewed_dims": o_bias(O_gpu, O_ref, tie, skew, O_ref_rounded),
+            "O_single_max_rows_skewed_dims": o_bias(O_gpu, O_ref, notie, skew, O_ref_rounded),
+            "delta_tie_rows": delta_bias(delta_gpu, d_round, dO, O_ref, tie),
+            "delta_single_max_rows": delta_bias(delta_gpu, d_round, dO, O_ref, notie),
+        }
+    return out
