@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="gpt2_small")
+    p.add_argument("--mode", type=int, default=1, choices=(1, 2),
+                   help="stabilised forward: 1 = online shift, 2 = exact final shift (two passes)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the host oracle leg (profiling runs)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -110,7 +112,7 @@ def main():
     stream = torch.cuda.current_stream()
     kw = dict(scale=w.scale, causal=w.causal)
 
-    def fwd(stabilise=True):
+    def fwd(stabilise=args.mode):
         nss.attn_fwd(q, k, v, o, lse, ties, pone, formed, stabilise=stabilise, beta=w.beta, stream=stream, **kw)
 
     def bwd_dq():
@@ -154,14 +156,18 @@ def main():
         per["bwd_dkdv"].append(ev[s][2].elapsed_time(ev[s][3]))
     us = {k2: float(np.mean(x)) * 1e3 for k2, x in per.items()}
 
-    # the plain (unstabilised) forward for comparison
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        fwd(stabilise=False)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    fwd_plain_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # every forward mode, for comparison (plain, online shift, exact final shift)
+    fwd_modes_us = {}
+    for name, mode in (("plain", 0), ("online_shift", 1), ("exact_shift", 2)):
+        for _ in range(3):
+            fwd(stabilise=mode)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fwd(stabilise=mode)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fwd_modes_us[name] = e0.elapsed_time(e1) * 1e3 / args.steps
 
     fwd_flops, bwd_flops = w.fwd_flops(), w.bwd_flops()
     pairs = w.visible_pairs()
@@ -201,7 +207,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "D": D, "causal": w.causal,
-                   "stabilise": True, "beta": w.beta, "global_batch": B, "seq_len": N,
+                   "stabilise": {1: "online shift", 2: "exact final shift"}[args.mode], "beta": w.beta,
+                   "global_batch": B, "seq_len": N,
                    "parallelism": "none (1 GPU)"},
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "peak_assumption": "2516.6 TFLOPS dense bf16 = 256 CU x 4096 flop/clk x 2.4 GHz",
@@ -210,7 +217,7 @@ def main():
         "bwd_us": us["bwd_dq"] + us["bwd_dkdv"],
         "fwd_tflops": fwd_flops / (us["fwd"] * 1e-6) / 1e12,
         "bwd_tflops": bwd_flops / ((us["bwd_dq"] + us["bwd_dkdv"]) * 1e-6) / 1e12,
-        "fwd_unstabilised_us": fwd_plain_us,
+        "fwd_modes_us": fwd_modes_us,
         "roofline": roofline,
         "cpu_baseline": None,
     }
@@ -244,7 +251,8 @@ def cpu_leg(w, d, nss, t, stream):
 
     gO = inputs_f64(d["dO"])
     res = {}
-    for stabilise in (False, True):
+    names = {0: "unstabilised", 1: "stabilised", 2: "stabilised_exact"}
+    for stabilise in (0, 1, 2):
         f = nss.forward(t["q"], t["k"], t["v"], scale=w.scale, causal=w.causal, stabilise=stabilise,
                         beta=w.beta, stream=stream)
         b = nss.backward(t["q"], t["k"], t["v"], f["o"], t["dO"], f["lse"], scale=w.scale,
@@ -260,9 +268,9 @@ def cpu_leg(w, d, nss, t, stream):
             "delta": float(np.max(np.abs(dl - rb["delta"]) / rb["tol_delta"]))}
         rep["pbar_one_events_on_tie_rows"] = int(f["pbar_one"].cpu().numpy()[ref["ties"] > 1].sum())
         rep["formed_ones_on_tie_rows"] = int(f["formed_ones"].cpu().numpy()[ref["ties"] > 1].sum())
-        res["stabilised" if stabilise else "unstabilised"] = rep
+        res[names[stabilise]] = rep
     res["O_mode_difference_z"] = bias.mode_difference(
-        res["stabilised"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"],
+        res["stabilised_exact"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"],
         res["unstabilised"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"])
     res["tie_rows"] = int((ref["ties"] > 1).sum())
     return cpu, res

@@ -63,8 +63,17 @@ typedef enum {
   ATTN_E_SCALE = -5,     /* scale not finite or not > 0                         */
   ATTN_E_ALIGN = -6,     /* a pointer is not 16-byte aligned                    */
   ATTN_E_ALIAS = -7,     /* an output overlaps an input or another output       */
-  ATTN_E_DEVICE = -9     /* not a gfx950 device, or a HIP launch failed         */
+  ATTN_E_DEVICE = -9,    /* not a gfx950 device, or a HIP launch failed         */
+  ATTN_E_MODE = -10      /* stabilise not 0, 1 or 2                             */
 } attn_status;
+
+/* Values of the `stabilise` argument. */
+enum {
+  ATTN_PLAIN = 0,        /* plain safe softmax: shift = running row max              */
+  ATTN_STAB_ONLINE = 1,  /* duplicate-max shift from the running (max, count)        */
+  ATTN_STAB_EXACT = 2    /* duplicate-max shift from the whole row's final (max,     */
+                         /* count): two passes, no transient P_bar == 1              */
+};
 
 /*
  * attn_fwd -- fused attention forward with the online (max, count) merge.
@@ -92,7 +101,21 @@ typedef enum {
  *                     equal to 1.0 the kernel actually fed to P_bar V (a tie
  *                     split across KV tiles forms one before its duplicate is
  *                     seen)
- *   stabilise    0 = plain safe softmax, 1 = duplicate-max shift
+ *   stabilise    ATTN_PLAIN (0): plain safe softmax, online.
+ *                ATTN_STAB_ONLINE (1): the duplicate-max shift, online: while a
+ *                tile is processed the shift follows the running (max, count),
+ *                so a duplicate that arrives in a later KV tile than the first
+ *                occurrence leaves one transient exact 1 in P_bar (rescaled
+ *                away afterwards; counted in formed_ones).
+ *                ATTN_STAB_EXACT (2): the duplicate-max shift from each row's
+ *                final (max, count): a first pass merges every KV tile of the
+ *                row (it writes ties and pbar_one, and keeps the shift in lse),
+ *                the second pass forms every P_bar entry once with that shift,
+ *                so no entry of a repeated-max row ever equals 1 (the rule of
+ *                the minimal-fix section applied to the whole row, as written),
+ *                and formed_ones counts exactly the entries whose bf16 rounding
+ *                is 1 under the final shift.
+ *                Other values: ATTN_E_MODE.
  *   beta         the rule's factor (> 1, finite) when stabilise != 0; ignored
  *                otherwise
  */
@@ -108,7 +131,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * delta_i = sum_c dO_ic O_ic (91haoming.cn/news/show-608006, section 三),
  * dP = dO V^T, dS = P o (dP - delta), dQ = scale dS K, dK = scale dS^T Q,
  * dV = P^T dO.  P is recomputed from the forward's lse, which carries the
- * forward's shift, so the arithmetic is the same in both modes; `stabilise`
+ * forward's shift, so the arithmetic is the same in every mode; `stabilise`
  * and `beta` are validated as for attn_fwd and otherwise unused.
  *
  *   q, k, v, o, dO  in   bf16 [B][H][N][D] (o from attn_fwd)

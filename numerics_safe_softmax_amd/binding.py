@@ -91,6 +91,14 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+PLAIN, STAB_ONLINE, STAB_EXACT = 0, 1, 2
+
+
+def _mode(stabilise) -> int:
+    """stabilise: False/0 plain, True/1 online duplicate-max shift, 2 exact final shift."""
+    return int(stabilise)
+
+
 def _shape(q):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, D]")
@@ -102,7 +110,7 @@ def attn_fwd(q, k, v, o, lse, ties=None, pbar_one=None, formed_ones=None, *, sca
     B, H, N, D = _shape(q)
     _check(lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ties), _ptr(pbar_one),
                           _ptr(formed_ones), B, H, N, D, float(scale), int(bool(causal)),
-                          int(bool(stabilise)), float(beta), _stream(stream)))
+                          _mode(stabilise), float(beta), _stream(stream)))
 
 
 def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, *, scale: float, causal: bool, stabilise: bool,
@@ -110,7 +118,7 @@ def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, *, scale: float, causal: bo
     B, H, N, D = _shape(q)
     _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
                           _ptr(dv), _ptr(delta), B, H, N, D, float(scale), int(bool(causal)),
-                          int(bool(stabilise)), float(beta), _stream(stream)))
+                          _mode(stabilise), float(beta), _stream(stream)))
 
 
 def attn_bwd_dq(q, k, v, o, dO, lse, dq, delta, *, scale: float, causal: bool, stream=None) -> None:

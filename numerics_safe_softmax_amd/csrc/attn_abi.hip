@@ -79,7 +79,7 @@ int launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_DEVICE; }
 
 extern "C" {
 
-int attn_abi_version(void) { return 1; }
+int attn_abi_version(void) { return 2; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -92,6 +92,7 @@ const char* attn_status_string(int status) {
     case ATTN_E_ALIGN: return "every pointer must be 16-byte aligned";
     case ATTN_E_ALIAS: return "an output overlaps an input or another output";
     case ATTN_E_DEVICE: return "not a gfx950 device, or a HIP launch failed";
+    case ATTN_E_MODE: return "stabilise must be 0 (plain), 1 (online shift) or 2 (exact final shift)";
     default: return "unknown attn_status";
   }
 }
@@ -101,6 +102,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int stabilise, float beta, void* stream) {
   bool empty = false;
   int st = check_scalars(B, H, N, D, scale, stabilise != 0, beta, &empty);
+  if (st == ATTN_OK && (stabilise < 0 || stabilise > 2)) st = ATTN_E_MODE;
   if (st != ATTN_OK || empty) return st;
   if (!q || !k || !v || !o || !lse) return ATTN_E_NULLPTR;
   const void* ptrs[] = {q, k, v, o, lse, ties, pbar_one, formed_ones};
@@ -110,8 +112,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   const Span out[] = {{o, tb}, {lse, rb}, {ties, rb}, {pbar_one, rb}, {formed_ones, rb}};
   if ((st = check_alias(in, 3, out, 5)) != ATTN_OK) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  nss::FwdArgs a{q, k, v, o, lse, ties, pbar_one, formed_ones, nullptr, B, H, N, D, scale,
-                 causal ? 1 : 0, stabilise ? 1 : 0, beta};
+  nss::FwdArgs a{q, k, v, o, lse, ties, pbar_one, formed_ones, nullptr, nullptr, B, H, N, D, scale,
+                 causal ? 1 : 0, stabilise, beta};
   return launched(nss::launch_fwd(a, (hipStream_t)stream));
 }
 
@@ -128,7 +130,7 @@ int attn_tiecount(const void* q, const void* k, int32_t* ties, float* rowmax, in
   const Span out[] = {{ties, rb}, {rowmax, rb}};
   if ((st = check_alias(in, 2, out, 2)) != ATTN_OK) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  nss::FwdArgs a{q, k, nullptr, nullptr, nullptr, ties, nullptr, nullptr, rowmax, B, H, N, D, scale,
+  nss::FwdArgs a{q, k, nullptr, nullptr, nullptr, ties, nullptr, nullptr, rowmax, nullptr, B, H, N, D, scale,
                  causal ? 1 : 0, 0, 2.f};
   return launched(nss::launch_tiecount(a, (hipStream_t)stream));
 }
@@ -174,6 +176,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int stabilise, float beta, void* stream) {
   bool empty = false;
   int st = check_scalars(B, H, N, D, scale, stabilise != 0, beta, &empty);
+  if (st == ATTN_OK && (stabilise < 0 || stabilise > 2)) st = ATTN_E_MODE;
   if (st != ATTN_OK || empty) return st;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !delta) return ATTN_E_NULLPTR;
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv, delta};

@@ -98,13 +98,17 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
 
 // ---------------------------------------------------------------------------
 // LDS tiles: R rows x D bf16, row-major, rows of D/8 16-byte chunks; chunk c
-// of row r sits at chunk c ^ (r & 7), so the eight rows a ds_read_b128 phase
-// touches land on distinct banks.
+// of row r sits at chunk c ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1).  The
+// eight rows one ds_read_b128 phase touches get eight different f (distinct
+// banks), and the four rows a ds_read_b64_tr_b16 group reads (32 bytes each,
+// an even/odd chunk pair) get pairs f = b, 2+b, 4+b, 6+b, whose chunk pairs
+// are disjoint (no bank conflict on 32 banks either).
 // ---------------------------------------------------------------------------
 template <int D>
 struct Tile {
   static constexpr int CPR = D / 8;
-  __device__ static __forceinline__ int chunk(int r, int c) { return r * CPR + (c ^ (r & 7)); }
+  __device__ static __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+  __device__ static __forceinline__ int chunk(int r, int c) { return r * CPR + (c ^ swz(r)); }
   // 8 bf16 of row r starting at column 8c (an MFMA A/B row operand)
   __device__ static __forceinline__ bf16x8 row8(const uint16_t* t, int r, int c) {
     return as_bf16x8(ld16(t + chunk(r, c) * 8));
@@ -139,7 +143,7 @@ __device__ __forceinline__ void tile_to_lds(const uint16_t* __restrict__ src, in
   for (int i = 0; i < PER; ++i) {
     const int P = i * 256 + wu * 64 + lane;
     const int r = P / CPR, p = P % CPR;
-    const int c = p ^ (r & 7);
+    const int c = p ^ Tile<D>::swz(r);
     int gr = r0 + r;
     gr = gr < N ? gr : N - 1;
     __builtin_amdgcn_global_load_lds(src + (size_t)gr * D + c * 8, (lds_void*)(tile + (i * 256 + wu * 64) * 8), 16,
@@ -192,8 +196,8 @@ template <int D, int BN, bool CAUSAL, bool TIES_ONLY>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int32_t* __restrict__ TIES,
-    int32_t* __restrict__ PONE, int32_t* __restrict__ FORMED, float* __restrict__ ROWMAX, int BH, int N,
-    float scale, int stabilise, float beta, int nqt) {
+    int32_t* __restrict__ PONE, int32_t* __restrict__ FORMED, float* __restrict__ ROWMAX,
+    float* __restrict__ SHIFT, int BH, int N, float scale, int stabilise, float beta, int nqt) {
   using F = Fwd<D, BN, CAUSAL, TIES_ONLY>;
   constexpr int BM = F::BM, NKB = F::NKB, NKK = F::NKK, NCB = F::NCB, TILE = F::TILE;
   constexpr int NT = TIES_ONLY ? 1 : 2;  // K (and V) per stage
@@ -337,8 +341,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   const size_t row = (size_t)bh * N + qi;
   if constexpr (TIES_ONLY) {
     if (h == 0 && qi < N) {
-      TIES[row] = c_run;
+      if (TIES) TIES[row] = c_run;
       if (ROWMAX) ROWMAX[row] = scale * m_run;
+      if (SHIFT || PONE) {  // first pass of the exact-final-shift forward
+        const float base = m_run * t;
+        const float m2 = shifted(m_run, c_run, base, stabilise, beta);
+        if (SHIFT) SHIFT[row] = m2;
+        if (PONE) PONE[row] = (__builtin_bit_cast(uint16_t, (__bf16)exp2f_fast(base - m2)) == 0x3F80) ? 1 : 0;
+      }
     }
   } else {
     const float ltot = sum32(lsum);
@@ -362,6 +372,139 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
         if (FORMED) FORMED[row] = ones_tot;
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward with the final shift known (second pass of the exact-final-shift
+// mode).  The first pass (fwd_kernel<..., TIES_ONLY>) has merged every KV tile
+// of each row into its final (max, count) and stored the shift m2 of the rule
+// in LSE[row] (log2-scaled units); here every P_bar entry is formed once, with
+// that shift, so no entry of a repeated-max row is ever rounded to 1 -- not
+// even transiently, as in the online kernel when a duplicate arrives in a later
+// tile -- and no rescaling is needed.  LSE[row] is then overwritten with the
+// natural-log log-sum-exp.
+// ---------------------------------------------------------------------------
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int32_t* __restrict__ FORMED, int BH, int N, float scale,
+    int nqt) {
+  constexpr int BM = 128, NKB = BN / 32, NKK = D / 16, NCB = D / 32, TILE = BN * D;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, h = lane >> 5;
+  int rank, bh;
+  map_block(blockIdx.x, BH, rank, bh);
+  const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
+  const size_t head = (size_t)bh * N * D;
+  const int q0 = qt * BM, qw = q0 + 32 * wu, qi = qw + li;
+  const size_t row = (size_t)bh * N + qi;
+  const float t = scale * kLog2e;
+
+  const int kend = CAUSAL ? min(q0 + BM, N) : N;
+  const int nkt = (kend + BN - 1) / BN;
+  auto fetch = [&](int kt, int buf) {
+    uint16_t* base = lds + buf * 2 * TILE;
+    tile_to_lds<BN, D>(K + head, kt * BN, N, base, wu, lane);
+    tile_to_lds<BN, D>(V + head, kt * BN, N, base + TILE, wu, lane);
+  };
+  bf16x8 qf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    qf[kk] = as_bf16x8(qi < N ? ld16(Q + head + (size_t)qi * D + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
+  const float m2 = qi < N ? LSE[row] : 0.f;
+  wait_vmem();
+  fetch(0, 0);
+
+  f32x16 oacc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) oacc[cb] = f32x16{};
+  float lsum = 0.f;
+  int ones = 0;
+  const bool count_ones = FORMED != nullptr;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < nkt) fetch(kt + 1, buf ^ 1);
+    const uint16_t* Kt = lds + buf * 2 * TILE;
+    const uint16_t* Vt = Kt + TILE;
+    const int k0 = kt * BN;
+    const bool active = qw < N && (!CAUSAL || k0 <= qw + 31);
+    if (!active) continue;
+
+    bf16x8 ka[NKB][NKK];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = Tile<D>::row8(Kt, 32 * kb + li, 2 * kk + h);
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma(ka[kb][kk], qf[kk], s[kb]);
+    bf16x8 va[NKB][2][NCB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) va[kb][m][cb] = Tile<D>::trans8(Vt, 32 * kb + 16 * m, cb, lane);
+    if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if ((CAUSAL && key > qi) || key >= N) s[kb][r] = -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f_fast(__builtin_fmaf(s[kb][r], t, -m2));
+        s[kb][r] = p;
+        lsum += p;
+      }
+    if (count_ones) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ones += (s[kb][r] >= kBf16OneLow) ? 1 : 0;
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const bf16x8 p0 = pack8(s[kb], 0), p1 = pack8(s[kb], 8);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        oacc[cb] = mfma(va[kb][0][cb], p0, oacc[cb]);
+        oacc[cb] = mfma(va[kb][1][cb], p1, oacc[cb]);
+      }
+    }
+  }
+
+  if (qw >= N) return;
+  const float ltot = sum32(lsum);
+  const int ones_tot = sum32i(ones);
+  const float inv = 1.0f / ltot;
+  if (qi >= N) return;
+  uint16_t* op = O + head + (size_t)qi * D;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      store_bf16x4(op + 32 * cb + 8 * g + 4 * h, oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv,
+                   oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
+  if (h == 0) {
+    LSE[row] = (m2 + __builtin_amdgcn_logf(ltot)) * kLn2;
+    if (FORMED) FORMED[row] = ones_tot;
   }
 }
 
@@ -632,7 +775,18 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   hipLaunchKernelGGL((fwd_kernel<D, kFwdBN, CAUSAL, TIES_ONLY>), dim3(nqt * BH), dim3(256), 0, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.ties, a.pbar_one, a.formed_ones, a.rowmax, BH, a.N, a.scale, a.stabilise, a.beta, nqt);
+                     a.ties, a.pbar_one, a.formed_ones, a.rowmax, a.shift, BH, a.N, a.scale, a.stabilise, a.beta,
+                     nqt);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_fixed_t(const FwdArgs& a, hipStream_t st) {
+  const int nqt = (a.N + 127) / 128;
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL((fwd_fixed_kernel<D, kFwdBN, CAUSAL>), dim3(nqt * BH), dim3(256), 0, st,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                     a.formed_ones, BH, a.N, a.scale, nqt);
   return hipGetLastError();
 }
 
@@ -642,7 +796,23 @@ static hipError_t launch_fwd_any(const FwdArgs& a, hipStream_t st) {
   return a.causal ? launch_fwd_t<128, true, TIES_ONLY>(a, st) : launch_fwd_t<128, false, TIES_ONLY>(a, st);
 }
 
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) { return launch_fwd_any<false>(a, st); }
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
+  if (a.stabilise != 2) return launch_fwd_any<false>(a, st);
+  // exact final shift: pass 1 merges each whole row into (max, count) and
+  // stores the rule's shift in LSE (plus ties and pbar_one); pass 2 forms
+  // P_bar once with that shift.
+  FwdArgs p1 = a;
+  p1.o = nullptr;
+  p1.formed_ones = nullptr;
+  p1.rowmax = nullptr;
+  p1.shift = a.lse;
+  p1.stabilise = 1;
+  hipError_t e = launch_fwd_any<true>(p1, st);
+  if (e != hipSuccess) return e;
+  if (a.D == 64) return a.causal ? launch_fwd_fixed_t<64, true>(a, st) : launch_fwd_fixed_t<64, false>(a, st);
+  return a.causal ? launch_fwd_fixed_t<128, true>(a, st) : launch_fwd_fixed_t<128, false>(a, st);
+}
+
 hipError_t launch_tiecount(const FwdArgs& a, hipStream_t st) { return launch_fwd_any<true>(a, st); }
 
 template <int D, bool CAUSAL>

@@ -12,9 +12,10 @@ struct FwdArgs {
   float* lse;
   int32_t *ties, *pbar_one, *formed_ones;
   float* rowmax;
+  float* shift;  // first pass of the exact-final-shift mode: the rule's shift per row
   int B, H, N, D;
   float scale;
-  int causal, stabilise;
+  int causal, stabilise;  // stabilise: 0 plain, 1 online duplicate-max shift, 2 exact final shift
   float beta;
 };
 

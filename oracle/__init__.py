@@ -47,8 +47,8 @@ class _Problem(ctypes.Structure):
 
 
 _FWD_FIELDS = ["O", "O_stab", "tol_O", "lse", "tol_lse", "rowmax", "shift", "pbar_max",
-               "ties", "pbar_one", "near_ones", "amb_tie", "amb_pbar", "flags"]
-_FWD_INT = {"ties", "pbar_one", "near_ones", "amb_tie", "amb_pbar", "flags"}
+               "ties", "pbar_one", "near_ones", "amb_tie", "amb_pbar", "amb_near", "flags"]
+_FWD_INT = {"ties", "pbar_one", "near_ones", "amb_tie", "amb_pbar", "amb_near", "flags"}
 _FWD_ROWWISE = {"O", "O_stab", "tol_O"}
 
 

@@ -276,6 +276,7 @@ typedef struct {
   int32_t* near_ones; /* [B][H][N] #keys with bf16_RNE(exp(S - m*)) == 1  */
   int32_t* amb_tie;   /* [B][H][N] tie count not decidable in fp32        */
   int32_t* amb_pbar;  /* [B][H][N] exp(rm - m*) at the bf16 1.0 boundary  */
+  int32_t* amb_near;  /* [B][H][N] some exp(S - m*) at the bf16 1.0 boundary */
   int32_t* flags;     /* [B][H][N] bit0 rm==0 tie, bit1 underflow, bit2 slow dots */
 } orc_fwd_out;
 
@@ -474,11 +475,12 @@ static void forward_row(const orc_problem* p, const decoded* dc, int64_t row, ro
   /* the fix's shift and the literal stabilised P_bar */
   const double mstar = orc_shift_rule(rm, rs, p->stabilise, p->beta);
   double ell_stab = 0.0;
-  int near = 0;
+  int near = 0, near_amb = 0;
   for (int j = 0; j <= jl; ++j) {
     double pb = exp(p->scale * s->raw[j] - mstar);
     ell_stab += pb;
     if (orc_bf16_from_double(pb, ORC_RNE) == BF16_ONE) ++near;
+    if (fabs(pb - (1.0 - 0x1p-9)) <= 0x1p-14) near_amb = 1;
   }
   const double pmax = exp(rm - mstar);
   const double nfac = (double)nvis * U_F32;
@@ -519,6 +521,7 @@ static void forward_row(const orc_problem* p, const decoded* dc, int64_t row, ro
   if (out->near_ones) out->near_ones[row] = near;
   if (out->amb_tie) out->amb_tie[row] = tie_ambiguous(p, bh, jl, s, rm_raw, rs);
   if (out->amb_pbar) out->amb_pbar[row] = fabs(pmax - (1.0 - 0x1p-9)) <= 0x1p-14;
+  if (out->amb_near) out->amb_near[row] = near_amb;
   if (out->flags) {
     int f = 0;
     if (rs > 1 && rm == 0.0) f |= 1;

@@ -7,8 +7,8 @@ import numpy as np
 import oracle
 from numerics_safe_softmax_amd import inputs
 
-FWD_WANT = ["O", "tol_O", "lse", "tol_lse", "ties", "pbar_one", "amb_tie", "amb_pbar", "near_ones",
-            "rowmax", "flags"]
+FWD_WANT = ["O", "tol_O", "lse", "tol_lse", "ties", "pbar_one", "amb_tie", "amb_pbar", "amb_near",
+            "near_ones", "rowmax", "flags"]
 
 
 def to_dev(d, dev):

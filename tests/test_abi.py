@@ -38,10 +38,10 @@ def test_exports_every_header_function():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5, -6, -7, -9):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -9, -10):
         assert binding.status_string(s) and binding.status_string(s) != "unknown attn_status"
     assert binding.status_string(12345) == "unknown attn_status"
-    assert binding.abi_version() == 1
+    assert binding.abi_version() == 2
 
 
 def fwd(**kw):
@@ -84,6 +84,8 @@ def test_forward_and_backward_validation(call):
     assert call(scale=float("inf")) == -5
     assert call(k=addr(1) + 8) == -6
     assert call(q=addr(0) + 2) == -6
+    assert call(stab=3) == -10
+    assert call(stab=-1) == -10
 
 
 def test_beta_ignored_when_not_stabilised():

@@ -1,4 +1,4 @@
-"""Signed-bias diagnostic and the P_bar == 1 event counts, both modes, on the GPU.
+"""Signed-bias diagnostic and the P_bar == 1 event counts, all three modes, on the GPU.
 
 itsolotime.com/archives/23922, section "机制解释二": repeated row maxima put
 exact 1s into P_bar (the trigger), and with negative-dominated V the bf16
@@ -40,11 +40,11 @@ def test_events_and_bias(wname, heads):
         hm[x // w.H, x % w.H] = True
     rmask = np.repeat(hm[:, :, None], w.N, axis=2)
     res, formed = {}, {}
-    for stabilise in (False, True):
+    for stabilise in (0, 1, 2):
         f = parity.gpu_forward(t, w, stabilise)
         b = parity.gpu_backward(t, w, f, stabilise)
         torch.cuda.synchronize()
-        ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=stabilise,
+        ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=stabilise != 0,
                              beta=w.beta, rows=rows, want=parity.FWD_WANT)
         rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=w.causal, heads=heads)
         tie = rmask & (ref["ties"] > 1)
@@ -56,7 +56,7 @@ def test_events_and_bias(wname, heads):
             assert int(pone[exact].sum()) == 0
         else:
             assert np.all(pone[rmask] == 1)
-            assert np.all(formed[False][exact] >= ref["ties"][exact])
+            assert np.all(formed[0][exact] >= ref["ties"][exact])
         O = parity.f64(f["o"])
         O_round = inputs.bits_to_float(oracle.bf16_from_double(np.nan_to_num(ref["O"]), "rne")).astype(np.float64)
         rep = bias.report(O, ref["O"], parity.f64(b["delta"]), rb["delta"],
@@ -65,10 +65,16 @@ def test_events_and_bias(wname, heads):
         rep["tie_rows"] = int(tie.sum())
         rep["pbar_one_events_on_tie_rows"] = int(pone[tie].sum())
         rep["formed_ones_on_tie_rows"] = int(formed[stabilise][tie].sum())
-        res["stabilised" if stabilise else "unstabilised"] = rep
-    # the shift is never below the plain one, so the stabilised kernel forms no
-    # more bf16 ones than the plain kernel on any row (same running max sequence)
-    assert np.all(formed[True][rmask] <= formed[False][rmask])
+        if stabilise == 2:
+            # no exact 1 is ever formed on a repeated-max row
+            exn = exact & (ref["amb_near"] == 0)
+            assert np.array_equal(formed[2][exn], ref["near_ones"][exn])
+        res[{0: "unstabilised", 1: "stabilised", 2: "stabilised_exact"}[stabilise]] = rep
+    # both stabilised shifts are never below the plain kernel's running max at any
+    # tile (online: same running max sequence; exact: the final max), so neither
+    # forms more bf16 ones than the plain kernel on any row
+    assert np.all(formed[1][rmask] <= formed[0][rmask])
+    assert np.all(formed[2][rmask] <= formed[0][rmask])
     res["O_mode_difference_z_vs_rounded"] = bias.mode_difference(
         res["stabilised"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"],
         res["unstabilised"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"])
@@ -77,9 +83,13 @@ def test_events_and_bias(wname, heads):
     if os.path.isdir(out):
         with open(os.path.join(out, "bias_report.json"), "w") as fh:
             json.dump(REPORT, fh, indent=1)
-    z = res["stabilised"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"]["z"]
-    print("  stabilised O bias z (vs rounded FP64) = %.2f; unstabilised %.2f; difference z %.2f" % (
-        z, res["unstabilised"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"]["z"],
-        res["O_mode_difference_z_vs_rounded"]), flush=True)
-    # "indistinguishable from zero": |z| < 3 for the stabilised O bias of the computation
-    assert abs(z) < 3.0
+    zs = {m: res[m]["vs_rounded_reference"]["O_tie_rows_skewed_dims"]["z"]
+          for m in ("unstabilised", "stabilised", "stabilised_exact")}
+    print("  O bias z on tie rows (vs rounded FP64): plain %.2f, online shift %.2f, exact shift %.2f" % (
+        zs["unstabilised"], zs["stabilised"], zs["stabilised_exact"]), flush=True)
+    # "indistinguishable from zero": |z| < 3 for the online stabilised O bias of
+    # the computation.  The exact-final-shift mode is reported, not held to it:
+    # on the ternary sink workload its P_bar values sit on a few grid points
+    # whose bf16 roundings do not cancel, and normalising by the fp32 row sum
+    # turns that into a bias whose sign follows the shift (see the bias report).
+    assert abs(zs["stabilised"]) < 3.0

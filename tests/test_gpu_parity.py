@@ -44,28 +44,35 @@ def _small_workload(B, H, N, D, causal, seed, tie_block):
                          v_skew_dims=D // 4, v_mu=-2.0, v_sigma=0.5, do_mu=-0.5)
 
 
-@pytest.mark.parametrize("stabilise", [False, True])
+MODES = [0, 1, 2]   # plain, online duplicate-max shift, exact final shift
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dH%dN%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
-def test_small_fwd_bwd_parity(case, stabilise):
+def test_small_fwd_bwd_parity(case, mode):
     w = _small_workload(*case)
-    _say("parity %s stabilise=%d" % (case, stabilise))
+    _say("parity %s mode=%d" % (case, mode))
     d = inputs.generate(w)
     t = parity.to_dev(d, DEV)
-    f = parity.gpu_forward(t, w, stabilise)
-    b = parity.gpu_backward(t, w, f, stabilise)
+    f = parity.gpu_forward(t, w, mode)
+    b = parity.gpu_backward(t, w, f, mode)
     torch.cuda.synchronize()
-    ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=stabilise,
+    ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=mode != 0,
                          beta=w.beta)
     rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=w.causal)
     fr = parity.check_forward(f, ref, label=str(case))
     br = parity.check_backward(b, rb, label=str(case))
     _say("  fwd %s bwd %s" % (fr, br))
-    # unstabilised rows: each tied maximum is fed to P_bar V as an exact bf16 1.0
     formed = f["formed_ones"].cpu().numpy()
     ok = ref["amb_tie"] == 0
-    if not stabilise:
+    if mode == 0:
+        # plain rows: each tied maximum is fed to P_bar V as an exact bf16 1.0
         assert np.all(formed[ok] >= ref["ties"][ok])
         assert np.all(f["pbar_one"].cpu().numpy() == 1)
+    if mode == 2:
+        # the exact-final-shift kernel forms exactly the bf16 ones the final shift predicts
+        okn = ok & (ref["amb_near"] == 0)
+        assert np.array_equal(formed[okn], ref["near_ones"][okn])
 
 
 @pytest.mark.parametrize("case", SMALL[:5], ids=lambda c: "B%dH%dN%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
@@ -75,10 +82,13 @@ def test_tiecount_parity(case):
     d = inputs.generate(w)
     t = parity.to_dev(d, DEV)
     r = nss.tiecount(t["q"], t["k"], scale=w.scale, causal=w.causal)
-    f = parity.gpu_forward(t, w, True)
+    f = parity.gpu_forward(t, w, 1)
+    f2 = parity.gpu_forward(t, w, 2)
     torch.cuda.synchronize()
     ref = oracle.forward(d["q"], d["k"], scale=w.scale, causal=w.causal,
                          want=["ties", "amb_tie", "rowmax"])
+    # both forward modes count the same duplicates as the detector
+    assert np.array_equal(f["ties"].cpu().numpy(), f2["ties"].cpu().numpy())
     ok = ref["amb_tie"] == 0
     ties = r["ties"].cpu().numpy()
     assert np.array_equal(ties[ok], ref["ties"][ok])
@@ -94,8 +104,8 @@ def test_deterministic_reruns():
     t = parity.to_dev(d, DEV)
     outs = []
     for _ in range(2):
-        f = parity.gpu_forward(t, w, True)
-        b = parity.gpu_backward(t, w, f, True)
+        f = parity.gpu_forward(t, w, 2)
+        b = parity.gpu_backward(t, w, f, 2)
         torch.cuda.synchronize()
         outs.append({k: v.cpu().clone() for k, v in list(f.items()) + list(b.items())})
     for k in outs[0]:
@@ -128,12 +138,12 @@ def test_workload_parity(wname, heads):
     for x in heads:
         hm[x // w.H, x % w.H] = True
     rmask = np.repeat(hm[:, :, None], w.N, axis=2)
-    for stabilise in (False, True):
+    for stabilise in MODES:
         f = parity.gpu_forward(t, w, stabilise)
         b = parity.gpu_backward(t, w, f, stabilise)
         torch.cuda.synchronize()
         ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal,
-                             stabilise=stabilise, beta=w.beta, rows=rows, want=parity.FWD_WANT)
+                             stabilise=stabilise != 0, beta=w.beta, rows=rows, want=parity.FWD_WANT)
         fr = parity.check_forward(f, ref, rows_mask=rmask, label="%s s=%d" % (wname, stabilise))
         rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=w.causal,
                              heads=heads)
@@ -143,3 +153,6 @@ def test_workload_parity(wname, heads):
         if stabilise:
             ok = tie & (ref["amb_tie"] == 0) & (ref["amb_pbar"] == 0) & ((ref["flags"] & 1) == 0)
             assert np.all(f["pbar_one"].cpu().numpy()[ok] == 0)
+        if stabilise == 2:
+            okn = rmask & (ref["amb_tie"] == 0) & (ref["amb_near"] == 0)
+            assert np.array_equal(f["formed_ones"].cpu().numpy()[okn], ref["near_ones"][okn])
