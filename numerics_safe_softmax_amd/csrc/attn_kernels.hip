@@ -38,6 +38,20 @@
 
 #include "attn_launch.h"
 
+// Tile and occupancy choices (compile-time; measured on MI355X).
+#ifndef NSS_DQ_WAVES
+#define NSS_DQ_WAVES 2
+#endif
+#ifndef NSS_DKDV_WAVES
+#define NSS_DKDV_WAVES 2
+#endif
+#ifndef NSS_DQ_BN
+#define NSS_DQ_BN 64
+#endif
+#ifndef NSS_DKDV_BQ
+#define NSS_DKDV_BQ 64
+#endif
+
 #ifndef NSS_FWD_STAGES
 #define NSS_FWD_STAGES 2
 #endif
@@ -514,7 +528,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
 // dQ^T += K^T dS^T.  One workgroup = 128 queries; KV tiles of BN keys.
 // ---------------------------------------------------------------------------
 template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ Og, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
     uint16_t* __restrict__ dQ, float* __restrict__ DELTA, int BH, int N, float scale, int nqt) {
@@ -625,7 +639,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 // dP = dO V^T, dS = P (dP - delta), dV^T += dO^T P, dK^T += Q^T dS.
 // ---------------------------------------------------------------------------
 template <int D, int BQ, bool CAUSAL>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale, int nkt) {
@@ -817,7 +831,7 @@ hipError_t launch_tiecount(const FwdArgs& a, hipStream_t st) { return launch_fwd
 
 template <int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
-  constexpr int BN = 64;
+  constexpr int BN = (D == 64 ? NSS_DQ_BN : 64);
   const int nqt = (a.N + 127) / 128;
   const int BH = a.B * a.H;
   hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL>), dim3(nqt * BH), dim3(256), 0, st, (const uint16_t*)a.q,
@@ -828,7 +842,7 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
-  constexpr int BQ = (D == 64 ? 64 : 32);
+  constexpr int BQ = (D == 64 ? NSS_DKDV_BQ : 32);
   const int nkt = (a.N + 127) / 128;
   const int BH = a.B * a.H;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, CAUSAL>), dim3(nkt * BH), dim3(256), 0, st, (const uint16_t*)a.q,
