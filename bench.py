@@ -3,14 +3,17 @@
 
 A step is one pass of the whole path over the GPT-2-small attention layer
 (B=8, H=12, N=1024, D=64, causal, bf16, synthetic seeded inputs with
-duplicate-max rows): attn_fwd (duplicate-max shift on, with its tie, P_bar == 1
-and formed-ones outputs) followed by attn_bwd (attn_bwd_dq then attn_bwd_dkdv).
-Inputs are resident in HBM before the timed region.  The reported value is
-algorithmic fwd+bwd TFLOPS (4 D + 10 D flops per visible query-key pair).
+duplicate-max rows): attn_fwd (duplicate-max shift on, with the rule's
+outputs: per-row duplicate count and the P_bar == 1 flag) followed by attn_bwd
+(attn_bwd_dq then attn_bwd_dkdv).  The optional per-row count of formed bf16
+ones is a diagnostic; its cost is reported beside the step.  Inputs are
+resident in HBM before the timed region.  The reported value is algorithmic
+fwd+bwd TFLOPS (4 D + 10 D flops per visible query-key pair).
 
 Printed: ONE JSON line with the metric, per-kernel HIP-event timings, the
-roofline of the dominant kernel and the FP64 oracle timed on the host (the
-cpu_baseline leg, which also yields the signed-bias diagnostic against FP64).
+roofline of the dominant kernel, a cold-cache variant, the other workload
+shapes, and the FP64 oracle timed on the host (the cpu_baseline leg, which also
+yields the signed-bias diagnostic against FP64).
 """
 from __future__ import annotations
 
@@ -43,6 +46,8 @@ def parse():
                    help="stabilised forward: 1 = online shift, 2 = exact final shift (two passes)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the host oracle leg (profiling runs)")
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="skip the timings of the other workload shapes and the cold-cache variant")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return p.parse_args()
@@ -112,8 +117,9 @@ def main():
     stream = torch.cuda.current_stream()
     kw = dict(scale=w.scale, causal=w.causal)
 
-    def fwd(stabilise=args.mode):
-        nss.attn_fwd(q, k, v, o, lse, ties, pone, formed, stabilise=stabilise, beta=w.beta, stream=stream, **kw)
+    def fwd(stabilise=args.mode, count_formed=False):
+        nss.attn_fwd(q, k, v, o, lse, ties, pone, formed if count_formed else None, stabilise=stabilise,
+                     beta=w.beta, stream=stream, **kw)
 
     def bwd_dq():
         nss.attn_bwd_dq(q, k, v, o, g, lse, dq, delta, stream=stream, **kw)
@@ -158,13 +164,14 @@ def main():
 
     # every forward mode, for comparison (plain, online shift, exact final shift)
     fwd_modes_us = {}
-    for name, mode in (("plain", 0), ("online_shift", 1), ("exact_shift", 2)):
+    for name, mode, cf in (("plain", 0, False), ("online_shift", 1, False), ("exact_shift", 2, False),
+                           ("online_shift_with_formed_ones_count", 1, True)):
         for _ in range(3):
-            fwd(stabilise=mode)
+            fwd(stabilise=mode, count_formed=cf)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
-            fwd(stabilise=mode)
+            fwd(stabilise=mode, count_formed=cf)
         e1.record(stream)
         torch.cuda.synchronize()
         fwd_modes_us[name] = e0.elapsed_time(e1) * 1e3 / args.steps
@@ -177,8 +184,8 @@ def main():
     tb = B * H * N * D * 2
     rb = B * H * N * 4
     kinfo = {
-        # S = QK^T and P_bar V: 4 D flops per visible pair; reads Q, K, V, writes O, LSE, 3 int rows
-        "fwd": (4.0 * D * pairs, 4 * tb + 4 * rb),
+        # S = QK^T and P_bar V: 4 D flops per visible pair; reads Q, K, V, writes O, LSE, 2 int rows
+        "fwd": (4.0 * D * pairs, 4 * tb + 3 * rb),
         # dQ = scale dS K: 2 D per pair (its S / dP recompute is overhead of the split);
         # reads Q, K, V, O, dO, LSE, writes dQ, delta
         "bwd_dq": (2.0 * D * pairs, 6 * tb + 2 * rb),
@@ -222,9 +229,91 @@ def main():
         "cpu_baseline": None,
     }
 
+    if not args.no_other_workloads:
+        out["cold_cache"] = cold_cache(t, w, nss, stream, args)
+        out["other_workloads"] = other_workloads(w.name, nss, stream, args.mode)
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["bias"] = cpu_leg(w, d, nss, t, stream)
     print(json.dumps(out), flush=True)
+
+
+def time_path(t, w, nss, stream, mode, reps, sets=None):
+    """Mean HIP-event microseconds of attn_fwd, attn_bwd_dq and attn_bwd_dkdv
+    over `reps` steps, rotating over the input sets given (default: one)."""
+    import numpy as np
+    import torch
+    sets = sets or [t]
+    B, H, N, D = w.B, w.H, w.N, w.D
+    dev = t["q"].device
+    bufs = []
+    for x in sets:
+        bufs.append({"o": torch.empty_like(x["q"]), "lse": torch.empty((B, H, N), dtype=torch.float32, device=dev),
+                     "ties": torch.empty((B, H, N), dtype=torch.int32, device=dev),
+                     "pone": torch.empty((B, H, N), dtype=torch.int32, device=dev),
+                     "dq": torch.empty_like(x["q"]), "dk": torch.empty_like(x["q"]), "dv": torch.empty_like(x["q"]),
+                     "delta": torch.empty((B, H, N), dtype=torch.float32, device=dev)})
+    kw = dict(scale=w.scale, causal=w.causal, stream=stream)
+
+    def run(i, ev=None):
+        x, b = sets[i % len(sets)], bufs[i % len(sets)]
+        if ev:
+            ev[0].record(stream)
+        nss.attn_fwd(x["q"], x["k"], x["v"], b["o"], b["lse"], b["ties"], b["pone"], None, stabilise=mode,
+                     beta=w.beta, **kw)
+        if ev:
+            ev[1].record(stream)
+        nss.attn_bwd_dq(x["q"], x["k"], x["v"], b["o"], x["dO"], b["lse"], b["dq"], b["delta"], **kw)
+        if ev:
+            ev[2].record(stream)
+        nss.attn_bwd_dkdv(x["q"], x["k"], x["v"], x["dO"], b["lse"], b["delta"], b["dk"], b["dv"], **kw)
+        if ev:
+            ev[3].record(stream)
+
+    for i in range(3 * len(sets)):
+        run(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for i in range(reps):
+        run(i, evs[i])
+    torch.cuda.synchronize()
+    us = {"fwd": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3,
+          "bwd_dq": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3,
+          "bwd_dkdv": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3}
+    fwd_us, bwd_us = us["fwd"], us["bwd_dq"] + us["bwd_dkdv"]
+    return {"kernels_us": us, "fwd_us": fwd_us, "bwd_us": bwd_us,
+            "fwd_tflops": w.fwd_flops() / (fwd_us * 1e-6) / 1e12,
+            "bwd_tflops": w.bwd_flops() / (bwd_us * 1e-6) / 1e12,
+            "fwd_bwd_tflops": (w.fwd_flops() + w.bwd_flops()) / ((fwd_us + bwd_us) * 1e-6) / 1e12}
+
+
+def cold_cache(t, w, nss, stream, args):
+    """The headline step rotating over 6 copies of the inputs (and outputs):
+    about 6 x 100 MB, more than the 256 MB last-level cache holds, so each
+    step starts with its operands in HBM only."""
+    sets = [{k2: x.clone() for k2, x in t.items()} for _ in range(6)]
+    r = time_path(t, w, nss, stream, args.mode, max(12, args.steps // 2), sets=sets)
+    r["input_sets"] = len(sets)
+    return r
+
+
+def other_workloads(skip, nss, stream, mode):
+    """fwd / bwd timings of the other synthetic workload shapes (parity-test
+    configurations; reported beside the headline, not part of its value)."""
+    import torch
+    from numerics_safe_softmax_amd import inputs
+    res = {}
+    for name in ("gpt2_medium", "long_context", "sink"):
+        if name == skip:
+            continue
+        w = inputs.WORKLOADS[name]
+        d = inputs.generate(w)
+        t = {k2: inputs.to_torch(x, torch.device("cuda:0")) for k2, x in d.items()}
+        r = time_path(t, w, nss, stream, mode, 10 if name == "long_context" else 20)
+        r["shape"] = "B%d H%d N%d D%d %s" % (w.B, w.H, w.N, w.D, "causal" if w.causal else "non-causal")
+        r["pct_of_bf16_peak"] = 100.0 * r["fwd_bwd_tflops"] / PEAK_BF16_TFLOPS
+        res[name] = r
+        del t
+    return res
 
 
 def cpu_leg(w, d, nss, t, stream):
