@@ -707,28 +707,23 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_ke
     const int r0 = qt * BQ;
     const bool active = kw < N && (!CAUSAL || r0 + BQ - 1 >= kw);
     if (active) {
-      f32x16 s[NQB], dp[NQB];
+      // one 32-query block at a time: S, dP, then P, dS, then dV, dK (halves
+      // the live score registers)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          s[qb] = mfma(Tile<D>::row8(Qt, 32 * qb + li, 2 * kk + h), kf[kk], s[qb]);
-          dp[qb] = mfma(Tile<D>::row8(Gt, 32 * qb + li, 2 * kk + h), vf[kk], dp[qb]);
+          s = mfma(Tile<D>::row8(Qt, 32 * qb + li, 2 * kk + h), kf[kk], s);
+          dp = mfma(Tile<D>::row8(Gt, 32 * qb + li, 2 * kk + h), vf[kk], dp);
         }
-      }
-      if ((CAUSAL && r0 < kw + 31) || r0 + BQ > N) {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
+        if ((CAUSAL && r0 + 32 * qb < kw + 31) || r0 + 32 * qb + 32 > N) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int qrow = r0 + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
-            if ((CAUSAL && qrow < kj) || qrow >= N) s[qb][r] = -INFINITY;
+            if ((CAUSAL && qrow < kj) || qrow >= N) s[r] = -INFINITY;
           }
-      }
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int rr = 32 * qb + 8 * g + 4 * h;
@@ -737,15 +732,13 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_ke
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int r = 4 * g + jj;
-            const float p = exp2f_fast(__builtin_fmaf(s[qb][r], t, -l4[jj]));
-            s[qb][r] = p;
-            dp[qb][r] = p * (dp[qb][r] - d4[jj]);
+            const float p = exp2f_fast(__builtin_fmaf(s[r], t, -l4[jj]));
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[jj]);
           }
         }
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const bf16x8 p0 = pack8(s[qb], 0), p1 = pack8(s[qb], 8);
-        const bf16x8 d0 = pack8(dp[qb], 0), d1 = pack8(dp[qb], 8);
+        const bf16x8 p0 = pack8(s, 0), p1 = pack8(s, 8);
+        const bf16x8 d0 = pack8(dp, 0), d1 = pack8(dp, 8);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           dva[cb] = mfma(Tile<D>::trans8(Gt, 32 * qb, cb, lane), p0, dva[cb]);
