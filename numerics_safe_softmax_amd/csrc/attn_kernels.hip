@@ -585,36 +585,29 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
     const bool active = qw < N && (!CAUSAL || k0 <= qw + 31);
     if (!active) continue;
 
-    f32x16 s[NKB], dp[NKB];
+    // one 32-key block at a time: S, dP, dS, then dQ (halves the live
+    // score registers)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        s[kb] = mfma(Tile<D>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
-        dp[kb] = mfma(Tile<D>::row8(Vt, 32 * kb + li, 2 * kk + h), gf[kk], dp[kb]);
+        s = mfma(Tile<D>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s);
+        dp = mfma(Tile<D>::row8(Vt, 32 * kb + li, 2 * kk + h), gf[kk], dp);
       }
-    }
-    if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      if ((CAUSAL && k0 + 32 * kb + 31 > qw) || k0 + 32 * kb + 32 > N) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          if ((CAUSAL && key > qi) || key >= N) s[kb][r] = -INFINITY;
+          if ((CAUSAL && key > qi) || key >= N) s[r] = -INFINITY;
         }
-    }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f_fast(__builtin_fmaf(s[kb][r], t, -lse2));
-        s[kb][r] = p * (dp[kb][r] - dl);
       }
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const bf16x8 d0 = pack8(s[kb], 0), d1 = pack8(s[kb], 8);
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f_fast(__builtin_fmaf(s[r], t, -lse2));
+        s[r] = p * (dp[r] - dl);
+      }
+      const bf16x8 d0 = pack8(s, 0), d1 = pack8(s, 8);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         dqa[cb] = mfma(Tile<D>::trans8(Kt, 32 * kb, cb, lane), d0, dqa[cb]);
