@@ -2,8 +2,9 @@
 stabilised safe softmax as a switchable mode.
 
 The compute lives in libattn.so (hand-written HIP, C ABI in include/attn.h);
-``binding`` marshals torch tensors to it; ``inputs`` generates the seeded
-synthetic workloads.
+``binding`` marshals torch tensors to it; ``autograd`` wraps it as a
+differentiable torch function and a GPT-2-shaped attention layer; ``inputs``
+generates the seeded synthetic workloads.
 """
 from .binding import (AttnError, abi_version, attn_bwd, attn_bwd_dkdv, attn_bwd_dq, attn_fwd,
                       attn_tiecount, backward, forward, status_string, tiecount)

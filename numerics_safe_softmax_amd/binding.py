@@ -81,7 +81,37 @@ def _ptr(t) -> Optional[int]:
         return None
     if not t.is_contiguous():
         raise ValueError("tensors passed to the C ABI must be contiguous")
+    if not t.is_cuda:
+        # the library dereferences device pointers only; a host pointer would fault the GPU
+        raise ValueError("tensors passed to the C ABI must live on the GPU (got %s)" % t.device)
     return t.data_ptr() or None
+
+
+def _expect(t, dtype, shape, name):
+    """dtype / shape check of one argument (None passes: optional outputs)."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _check_args(q, mats=(), rows=(), ints=()):
+    """bf16 [B, H, N, D] matrices, fp32 and int32 [B, H, N] row vectors, one device."""
+    import torch
+    B, H, N, D = _shape(q)
+    _expect(q, torch.bfloat16, (B, H, N, D), "q")
+    for name, t in mats:
+        _expect(t, torch.bfloat16, (B, H, N, D), name)
+    for name, t in rows:
+        _expect(t, torch.float32, (B, H, N), name)
+    for name, t in ints:
+        _expect(t, torch.int32, (B, H, N), name)
+    for name, t in list(mats) + list(rows) + list(ints):
+        if t is not None and t.device != q.device:
+            raise ValueError("%s is on %s, q on %s" % (name, t.device, q.device))
+    return B, H, N, D
 
 
 def _stream(stream) -> Optional[int]:
@@ -107,7 +137,8 @@ def _shape(q):
 
 def attn_fwd(q, k, v, o, lse, ties=None, pbar_one=None, formed_ones=None, *, scale: float,
              causal: bool, stabilise: bool, beta: float = 2.0, stream=None) -> None:
-    B, H, N, D = _shape(q)
+    B, H, N, D = _check_args(q, mats=(("k", k), ("v", v), ("o", o)), rows=(("lse", lse),),
+                             ints=(("ties", ties), ("pbar_one", pbar_one), ("formed_ones", formed_ones)))
     _check(lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ties), _ptr(pbar_one),
                           _ptr(formed_ones), B, H, N, D, float(scale), int(bool(causal)),
                           _mode(stabilise), float(beta), _stream(stream)))
@@ -115,26 +146,29 @@ def attn_fwd(q, k, v, o, lse, ties=None, pbar_one=None, formed_ones=None, *, sca
 
 def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, *, scale: float, causal: bool, stabilise: bool,
              beta: float = 2.0, stream=None) -> None:
-    B, H, N, D = _shape(q)
+    B, H, N, D = _check_args(q, mats=(("k", k), ("v", v), ("o", o), ("dO", dO), ("dq", dq), ("dk", dk),
+                                      ("dv", dv)), rows=(("lse", lse), ("delta", delta)))
     _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
                           _ptr(dv), _ptr(delta), B, H, N, D, float(scale), int(bool(causal)),
                           _mode(stabilise), float(beta), _stream(stream)))
 
 
 def attn_bwd_dq(q, k, v, o, dO, lse, dq, delta, *, scale: float, causal: bool, stream=None) -> None:
-    B, H, N, D = _shape(q)
+    B, H, N, D = _check_args(q, mats=(("k", k), ("v", v), ("o", o), ("dO", dO), ("dq", dq)),
+                             rows=(("lse", lse), ("delta", delta)))
     _check(lib().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq),
                              _ptr(delta), B, H, N, D, float(scale), int(bool(causal)), _stream(stream)))
 
 
 def attn_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, *, scale: float, causal: bool, stream=None) -> None:
-    B, H, N, D = _shape(q)
+    B, H, N, D = _check_args(q, mats=(("k", k), ("v", v), ("dO", dO), ("dk", dk), ("dv", dv)),
+                             rows=(("lse", lse), ("delta", delta)))
     _check(lib().attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(dk),
                                _ptr(dv), B, H, N, D, float(scale), int(bool(causal)), _stream(stream)))
 
 
 def attn_tiecount(q, k, ties, rowmax=None, *, scale: float, causal: bool, stream=None) -> None:
-    B, H, N, D = _shape(q)
+    B, H, N, D = _check_args(q, mats=(("k", k),), rows=(("rowmax", rowmax),), ints=(("ties", ties),))
     _check(lib().attn_tiecount(_ptr(q), _ptr(k), _ptr(ties), _ptr(rowmax), B, H, N, D, float(scale),
                                int(bool(causal)), _stream(stream)))
 
