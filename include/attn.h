@@ -125,6 +125,25 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              float beta, void* stream);
 
 /*
+ * attn_fwd_o32 -- attn_fwd that also returns O before its bf16 rounding.
+ *
+ * itsolotime.com/archives/23922, section "核心发现": training is stable again
+ * once the P behind dP comes from a path of higher precision (or a
+ * numerically equivalent, different one).  In this backward the forward's
+ * rounding reaches dS = P o (dP - delta) through delta = rowsum(dO o O)
+ * (91haoming.cn/news/show-608006, section 三); the fp32 O written here lets
+ * attn_bwd_o32 form delta without O's bf16 rounding.  Everything else, the
+ * arguments included, is as attn_fwd.
+ *
+ *   o32   out  fp32 [B][H][N][D]: O = O_acc / l before rounding to bf16
+ *              (o holds the same values rounded to nearest even)
+ */
+int attn_fwd_o32(const void* q, const void* k, const void* v, void* o, float* o32, float* lse,
+                 int32_t* ties, int32_t* pbar_one, int32_t* formed_ones,
+                 int B, int H, int N, int D, float scale, int causal, int stabilise,
+                 float beta, void* stream);
+
+/*
  * attn_bwd -- gradient of sum(dO * O) with respect to q, k and v.
  *
  * Runs attn_bwd_dq then attn_bwd_dkdv on `stream`.  With P = exp(S - lse):
@@ -143,6 +162,18 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv, float* delta,
              int B, int H, int N, int D, float scale, int causal, int stabilise,
              float beta, void* stream);
+
+/*
+ * attn_bwd_o32 -- attn_bwd with delta_i = sum_c dO_ic O_ic taken from the fp32
+ * O of attn_fwd_o32 (the high-precision delta path; see attn_fwd_o32).  dQ,
+ * dK and dV follow from that delta exactly as in attn_bwd.
+ *
+ *   o32   in   fp32 [B][H][N][D] from attn_fwd_o32; other arguments as attn_bwd
+ */
+int attn_bwd_o32(const void* q, const void* k, const void* v, const float* o32, const void* dO,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta,
+                 int B, int H, int N, int D, float scale, int causal, int stabilise,
+                 float beta, void* stream);
 
 /*
  * attn_bwd_dq -- first half of attn_bwd: delta and dQ, one pass per query

@@ -23,7 +23,9 @@ _F = ctypes.c_float
 
 _SIGS = {
     "attn_fwd": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _F, _P],
+    "attn_fwd_o32": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _F, _P],
     "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _F, _P],
+    "attn_bwd_o32": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _F, _P],
     "attn_bwd_dq": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P],
     "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P],
     "attn_tiecount": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P],
@@ -144,6 +146,28 @@ def attn_fwd(q, k, v, o, lse, ties=None, pbar_one=None, formed_ones=None, *, sca
                           _mode(stabilise), float(beta), _stream(stream)))
 
 
+def attn_fwd_o32(q, k, v, o, o32, lse, ties=None, pbar_one=None, formed_ones=None, *, scale: float,
+                 causal: bool, stabilise: bool, beta: float = 2.0, stream=None) -> None:
+    import torch
+    B, H, N, D = _check_args(q, mats=(("k", k), ("v", v), ("o", o)), rows=(("lse", lse),),
+                             ints=(("ties", ties), ("pbar_one", pbar_one), ("formed_ones", formed_ones)))
+    _expect(o32, torch.float32, (B, H, N, D), "o32")
+    _check(lib().attn_fwd_o32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o32), _ptr(lse), _ptr(ties),
+                              _ptr(pbar_one), _ptr(formed_ones), B, H, N, D, float(scale), int(bool(causal)),
+                              _mode(stabilise), float(beta), _stream(stream)))
+
+
+def attn_bwd_o32(q, k, v, o32, dO, lse, dq, dk, dv, delta, *, scale: float, causal: bool, stabilise: bool,
+                 beta: float = 2.0, stream=None) -> None:
+    import torch
+    B, H, N, D = _check_args(q, mats=(("k", k), ("v", v), ("dO", dO), ("dq", dq), ("dk", dk), ("dv", dv)),
+                             rows=(("lse", lse), ("delta", delta)))
+    _expect(o32, torch.float32, (B, H, N, D), "o32")
+    _check(lib().attn_bwd_o32(_ptr(q), _ptr(k), _ptr(v), _ptr(o32), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), _ptr(delta), B, H, N, D, float(scale), int(bool(causal)),
+                              _mode(stabilise), float(beta), _stream(stream)))
+
+
 def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, *, scale: float, causal: bool, stabilise: bool,
              beta: float = 2.0, stream=None) -> None:
     B, H, N, D = _check_args(q, mats=(("k", k), ("v", v), ("o", o), ("dO", dO), ("dq", dq), ("dk", dk),
@@ -177,7 +201,8 @@ def attn_tiecount(q, k, ties, rowmax=None, *, scale: float, causal: bool, stream
 # Allocation of outputs with torch, then one call of the entry point above.
 
 def forward(q, k, v, *, scale: float, causal: bool, stabilise: bool, beta: float = 2.0,
-            diagnostics: bool = True, stream=None) -> dict:
+            diagnostics: bool = True, o32: bool = False, stream=None) -> dict:
+    """attn_fwd (or attn_fwd_o32 with o32=True, adding the fp32 O as "o32")."""
     import torch
     B, H, N, D = _shape(q)
     dev = q.device
@@ -185,19 +210,30 @@ def forward(q, k, v, *, scale: float, causal: bool, stabilise: bool, beta: float
     if diagnostics:
         for f in ("ties", "pbar_one", "formed_ones"):
             out[f] = torch.empty((B, H, N), dtype=torch.int32, device=dev)
-    attn_fwd(q, k, v, out["o"], out["lse"], out.get("ties"), out.get("pbar_one"), out.get("formed_ones"),
-             scale=scale, causal=causal, stabilise=stabilise, beta=beta, stream=stream)
+    if o32:
+        out["o32"] = torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+        attn_fwd_o32(q, k, v, out["o"], out["o32"], out["lse"], out.get("ties"), out.get("pbar_one"),
+                     out.get("formed_ones"), scale=scale, causal=causal, stabilise=stabilise, beta=beta,
+                     stream=stream)
+    else:
+        attn_fwd(q, k, v, out["o"], out["lse"], out.get("ties"), out.get("pbar_one"), out.get("formed_ones"),
+                 scale=scale, causal=causal, stabilise=stabilise, beta=beta, stream=stream)
     return out
 
 
 def backward(q, k, v, o, dO, lse, *, scale: float, causal: bool, stabilise: bool = False,
-             beta: float = 2.0, stream=None) -> dict:
+             beta: float = 2.0, o32=None, stream=None) -> dict:
+    """attn_bwd (or attn_bwd_o32 when the fp32 O is given: delta from it)."""
     import torch
     B, H, N, D = _shape(q)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(q), "dv": torch.empty_like(q),
            "delta": torch.empty((B, H, N), dtype=torch.float32, device=q.device)}
-    attn_bwd(q, k, v, o, dO, lse, out["dq"], out["dk"], out["dv"], out["delta"], scale=scale,
-             causal=causal, stabilise=stabilise, beta=beta, stream=stream)
+    if o32 is not None:
+        attn_bwd_o32(q, k, v, o32, dO, lse, out["dq"], out["dk"], out["dv"], out["delta"], scale=scale,
+                     causal=causal, stabilise=stabilise, beta=beta, stream=stream)
+    else:
+        attn_bwd(q, k, v, o, dO, lse, out["dq"], out["dk"], out["dv"], out["delta"], scale=scale,
+                 causal=causal, stabilise=stabilise, beta=beta, stream=stream)
     return out
 
 

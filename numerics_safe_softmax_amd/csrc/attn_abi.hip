@@ -79,7 +79,7 @@ int launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_DEVICE; }
 
 extern "C" {
 
-int attn_abi_version(void) { return 2; }
+int attn_abi_version(void) { return 3; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -112,7 +112,27 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   const Span out[] = {{o, tb}, {lse, rb}, {ties, rb}, {pbar_one, rb}, {formed_ones, rb}};
   if ((st = check_alias(in, 3, out, 5)) != ATTN_OK) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  nss::FwdArgs a{q, k, v, o, lse, ties, pbar_one, formed_ones, nullptr, nullptr, B, H, N, D, scale,
+  nss::FwdArgs a{q, k, v, o, nullptr, lse, ties, pbar_one, formed_ones, nullptr, nullptr, B, H, N, D, scale,
+                 causal ? 1 : 0, stabilise, beta};
+  return launched(nss::launch_fwd(a, (hipStream_t)stream));
+}
+
+int attn_fwd_o32(const void* q, const void* k, const void* v, void* o, float* o32, float* lse, int32_t* ties,
+                 int32_t* pbar_one, int32_t* formed_ones, int B, int H, int N, int D, float scale, int causal,
+                 int stabilise, float beta, void* stream) {
+  bool empty = false;
+  int st = check_scalars(B, H, N, D, scale, stabilise != 0, beta, &empty);
+  if (st == ATTN_OK && (stabilise < 0 || stabilise > 2)) st = ATTN_E_MODE;
+  if (st != ATTN_OK || empty) return st;
+  if (!q || !k || !v || !o || !o32 || !lse) return ATTN_E_NULLPTR;
+  const void* ptrs[] = {q, k, v, o, o32, lse, ties, pbar_one, formed_ones};
+  if ((st = check_align(ptrs, 9)) != ATTN_OK) return st;
+  const size_t tb = (size_t)B * H * N * D * 2, rb = (size_t)B * H * N * 4;
+  const Span in[] = {{q, tb}, {k, tb}, {v, tb}};
+  const Span out[] = {{o, tb}, {o32, 2 * tb}, {lse, rb}, {ties, rb}, {pbar_one, rb}, {formed_ones, rb}};
+  if ((st = check_alias(in, 3, out, 6)) != ATTN_OK) return st;
+  if ((st = check_device()) != ATTN_OK) return st;
+  nss::FwdArgs a{q, k, v, o, o32, lse, ties, pbar_one, formed_ones, nullptr, nullptr, B, H, N, D, scale,
                  causal ? 1 : 0, stabilise, beta};
   return launched(nss::launch_fwd(a, (hipStream_t)stream));
 }
@@ -130,8 +150,8 @@ int attn_tiecount(const void* q, const void* k, int32_t* ties, float* rowmax, in
   const Span out[] = {{ties, rb}, {rowmax, rb}};
   if ((st = check_alias(in, 2, out, 2)) != ATTN_OK) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  nss::FwdArgs a{q, k, nullptr, nullptr, nullptr, ties, nullptr, nullptr, rowmax, nullptr, B, H, N, D, scale,
-                 causal ? 1 : 0, 0, 2.f};
+  nss::FwdArgs a{q, k, nullptr, nullptr, nullptr, nullptr, ties, nullptr, nullptr, rowmax, nullptr, B, H, N, D,
+                 scale, causal ? 1 : 0, 0, 2.f};
   return launched(nss::launch_tiecount(a, (hipStream_t)stream));
 }
 
@@ -148,7 +168,7 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, cons
   const Span out[] = {{dq, tb}, {delta, rb}};
   if ((st = check_alias(in, 6, out, 2)) != ATTN_OK) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  nss::BwdArgs a{q, k, v, o, dO, lse, dq, nullptr, nullptr, delta, B, H, N, D, scale, causal ? 1 : 0};
+  nss::BwdArgs a{q, k, v, o, dO, nullptr, lse, dq, nullptr, nullptr, delta, B, H, N, D, scale, causal ? 1 : 0};
   return launched(nss::launch_bwd_dq(a, (hipStream_t)stream));
 }
 
@@ -166,7 +186,7 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, c
   const Span out[] = {{dk, tb}, {dv, tb}};
   if ((st = check_alias(in, 6, out, 2)) != ATTN_OK) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  nss::BwdArgs a{q, k, v, nullptr, dO, lse, nullptr, dk, dv, const_cast<float*>(delta), B, H, N, D, scale,
+  nss::BwdArgs a{q, k, v, nullptr, dO, nullptr, lse, nullptr, dk, dv, const_cast<float*>(delta), B, H, N, D, scale,
                  causal ? 1 : 0};
   return launched(nss::launch_bwd_dkdv(a, (hipStream_t)stream));
 }
@@ -186,7 +206,27 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   const Span out[] = {{dq, tb}, {dk, tb}, {dv, tb}, {delta, rb}};
   if ((st = check_alias(in, 6, out, 4)) != ATTN_OK) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  nss::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, delta, B, H, N, D, scale, causal ? 1 : 0};
+  nss::BwdArgs a{q, k, v, o, dO, nullptr, lse, dq, dk, dv, delta, B, H, N, D, scale, causal ? 1 : 0};
+  if ((st = launched(nss::launch_bwd_dq(a, (hipStream_t)stream))) != ATTN_OK) return st;
+  return launched(nss::launch_bwd_dkdv(a, (hipStream_t)stream));
+}
+
+int attn_bwd_o32(const void* q, const void* k, const void* v, const float* o32, const void* dO, const float* lse,
+                 void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int D, float scale, int causal,
+                 int stabilise, float beta, void* stream) {
+  bool empty = false;
+  int st = check_scalars(B, H, N, D, scale, stabilise != 0, beta, &empty);
+  if (st == ATTN_OK && (stabilise < 0 || stabilise > 2)) st = ATTN_E_MODE;
+  if (st != ATTN_OK || empty) return st;
+  if (!q || !k || !v || !o32 || !dO || !lse || !dq || !dk || !dv || !delta) return ATTN_E_NULLPTR;
+  const void* ptrs[] = {q, k, v, o32, dO, lse, dq, dk, dv, delta};
+  if ((st = check_align(ptrs, 10)) != ATTN_OK) return st;
+  const size_t tb = (size_t)B * H * N * D * 2, rb = (size_t)B * H * N * 4;
+  const Span in[] = {{q, tb}, {k, tb}, {v, tb}, {o32, 2 * tb}, {dO, tb}, {lse, rb}};
+  const Span out[] = {{dq, tb}, {dk, tb}, {dv, tb}, {delta, rb}};
+  if ((st = check_alias(in, 6, out, 4)) != ATTN_OK) return st;
+  if ((st = check_device()) != ATTN_OK) return st;
+  nss::BwdArgs a{q, k, v, nullptr, dO, o32, lse, dq, dk, dv, delta, B, H, N, D, scale, causal ? 1 : 0};
   if ((st = launched(nss::launch_bwd_dq(a, (hipStream_t)stream))) != ATTN_OK) return st;
   return launched(nss::launch_bwd_dkdv(a, (hipStream_t)stream));
 }

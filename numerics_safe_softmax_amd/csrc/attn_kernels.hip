@@ -188,6 +188,10 @@ __device__ __forceinline__ float shifted(float m, int c, float base, int stabili
   return base;
 }
 
+__device__ __forceinline__ void store_f32x4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
 __device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, float c, float d) {
   bf16x2 x = __builtin_convertvector(f32x2{a, b}, bf16x2);
   bf16x2 y = __builtin_convertvector(f32x2{c, d}, bf16x2);
@@ -209,7 +213,7 @@ struct Fwd {
 template <int D, int BN, bool CAUSAL, bool TIES_ONLY>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int32_t* __restrict__ TIES,
+    uint16_t* __restrict__ O, float* __restrict__ O32, float* __restrict__ LSE, int32_t* __restrict__ TIES,
     int32_t* __restrict__ PONE, int32_t* __restrict__ FORMED, float* __restrict__ ROWMAX,
     float* __restrict__ SHIFT, int BH, int N, float scale, int stabilise, float beta, int nqt) {
   using F = Fwd<D, BN, CAUSAL, TIES_ONLY>;
@@ -376,6 +380,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
         for (int g = 0; g < 4; ++g)
           store_bf16x4(op + 32 * cb + 8 * g + 4 * h, oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv,
                        oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
+      if (O32) {  // O before its bf16 rounding (the high-precision delta path)
+        float* op32 = O32 + head + (size_t)qi * D;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            store_f32x4(op32 + 32 * cb + 8 * g + 4 * h, oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv,
+                        oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
+      }
       if (h == 0) {
         LSE[row] = (m2_run + __builtin_amdgcn_logf(ltot)) * kLn2;
         if (TIES) TIES[row] = c_run;
@@ -402,7 +415,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 template <int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int32_t* __restrict__ FORMED, int BH, int N, float scale,
+    uint16_t* __restrict__ O, float* __restrict__ O32, float* __restrict__ LSE, int32_t* __restrict__ FORMED, int BH,
+    int N, float scale,
     int nqt) {
   constexpr int BM = 128, NKB = BN / 32, NKK = D / 16, NCB = D / 32, TILE = BN * D;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];
@@ -516,6 +530,15 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
     for (int g = 0; g < 4; ++g)
       store_bf16x4(op + 32 * cb + 8 * g + 4 * h, oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv,
                    oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
+  if (O32) {
+    float* op32 = O32 + head + (size_t)qi * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store_f32x4(op32 + 32 * cb + 8 * g + 4 * h, oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv,
+                    oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
+  }
   if (h == 0) {
     LSE[row] = (m2 + __builtin_amdgcn_logf(ltot)) * kLn2;
     if (FORMED) FORMED[row] = ones_tot;
@@ -527,10 +550,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
 // S^T = K Q^T, P = exp2(S t - lse2), dP^T = V dO^T, dS = P (dP - delta),
 // dQ^T += K^T dS^T.  One workgroup = 128 queries; KV tiles of BN keys.
 // ---------------------------------------------------------------------------
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, bool O32>
 __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ Og, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+    const void* __restrict__ Og, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
     uint16_t* __restrict__ dQ, float* __restrict__ DELTA, int BH, int N, float scale, int nqt) {
   constexpr int BM = 128, NKB = BN / 32, NKK = D / 16, NCB = D / 32, TILE = BN * D;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];
@@ -562,9 +585,17 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
     const u32x4 z{0, 0, 0, 0};
     qf[kk] = as_bf16x8(qi < N ? ld16(Q + off) : z);
     gf[kk] = as_bf16x8(qi < N ? ld16(dO + off) : z);
-    const bf16x8 of = as_bf16x8(qi < N ? ld16(Og + off) : z);
+    if constexpr (O32) {  // delta from O before its bf16 rounding
+      const float* o32 = static_cast<const float*>(Og) + off;
+      const f32x4 a = qi < N ? *reinterpret_cast<const f32x4*>(o32) : f32x4{};
+      const f32x4 b = qi < N ? *reinterpret_cast<const f32x4*>(o32 + 4) : f32x4{};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dl += (float)gf[kk][e] * (float)of[e];
+      for (int e = 0; e < 4; ++e) dl += (float)gf[kk][e] * a[e] + (float)gf[kk][e + 4] * b[e];
+    } else {
+      const bf16x8 of = as_bf16x8(qi < N ? ld16(static_cast<const uint16_t*>(Og) + off) : z);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dl += (float)gf[kk][e] * (float)of[e];
+    }
   }
   dl = sum32(dl);
   const float lse2 = qi < N ? LSE[(size_t)bh * N + qi] * kLog2e : 0.f;
@@ -774,9 +805,9 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int nqt = (a.N + 127) / 128;
   const int BH = a.B * a.H;
   hipLaunchKernelGGL((fwd_kernel<D, kFwdBN, CAUSAL, TIES_ONLY>), dim3(nqt * BH), dim3(256), 0, st,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.ties, a.pbar_one, a.formed_ones, a.rowmax, a.shift, BH, a.N, a.scale, a.stabilise, a.beta,
-                     nqt);
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.o32,
+                     a.lse, a.ties, a.pbar_one, a.formed_ones, a.rowmax, a.shift, BH, a.N, a.scale, a.stabilise,
+                     a.beta, nqt);
   return hipGetLastError();
 }
 
@@ -785,8 +816,8 @@ static hipError_t launch_fwd_fixed_t(const FwdArgs& a, hipStream_t st) {
   const int nqt = (a.N + 127) / 128;
   const int BH = a.B * a.H;
   hipLaunchKernelGGL((fwd_fixed_kernel<D, kFwdBN, CAUSAL>), dim3(nqt * BH), dim3(256), 0, st,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.formed_ones, BH, a.N, a.scale, nqt);
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.o32,
+                     a.lse, a.formed_ones, BH, a.N, a.scale, nqt);
   return hipGetLastError();
 }
 
@@ -803,6 +834,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   // P_bar once with that shift.
   FwdArgs p1 = a;
   p1.o = nullptr;
+  p1.o32 = nullptr;
   p1.formed_ones = nullptr;
   p1.rowmax = nullptr;
   p1.shift = a.lse;
@@ -820,9 +852,14 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   constexpr int BN = (D == 64 ? NSS_DQ_BN : 64);
   const int nqt = (a.N + 127) / 128;
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL>), dim3(nqt * BH), dim3(256), 0, st, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o, (const uint16_t*)a.dO,
-                     a.lse, (uint16_t*)a.dq, a.delta, BH, a.N, a.scale, nqt);
+  if (a.o32)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL, true>), dim3(nqt * BH), dim3(256), 0, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const void*)a.o32, (const uint16_t*)a.dO,
+                       a.lse, (uint16_t*)a.dq, a.delta, BH, a.N, a.scale, nqt);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL, false>), dim3(nqt * BH), dim3(256), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, (const uint16_t*)a.dO,
+                       a.lse, (uint16_t*)a.dq, a.delta, BH, a.N, a.scale, nqt);
   return hipGetLastError();
 }
 

@@ -9,6 +9,7 @@ namespace nss {
 struct FwdArgs {
   const void *q, *k, *v;
   void* o;
+  float* o32;  // optional: O before its bf16 rounding, fp32 [B][H][N][D]
   float* lse;
   int32_t *ties, *pbar_one, *formed_ones;
   float* rowmax;
@@ -21,6 +22,7 @@ struct FwdArgs {
 
 struct BwdArgs {
   const void *q, *k, *v, *o, *dO;
+  const float* o32;  // optional: delta from this fp32 O instead of o
   const float* lse;
   void *dq, *dk, *dv;
   float* delta;

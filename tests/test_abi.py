@@ -28,7 +28,8 @@ def lib():
 
 def test_exports_every_header_function():
     names = binding.header_functions()
-    assert set(names) >= {"attn_fwd", "attn_bwd", "attn_tiecount", "attn_status_string"}
+    assert set(names) >= {"attn_fwd", "attn_bwd", "attn_tiecount", "attn_status_string", "attn_fwd_o32",
+                          "attn_bwd_o32", "attn_bwd_dq", "attn_bwd_dkdv", "attn_abi_version"}
     L = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(L, n), n
@@ -41,7 +42,7 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -9, -10):
         assert binding.status_string(s) and binding.status_string(s) != "unknown attn_status"
     assert binding.status_string(12345) == "unknown attn_status"
-    assert binding.abi_version() == 2
+    assert binding.abi_version() == 3
 
 
 def fwd(**kw):
@@ -125,3 +126,37 @@ def test_tiecount_and_split_backward_validation():
     bad = list(args)
     bad[7] = addr(0)
     assert L.attn_bwd_dkdv(*bad) == -7
+
+
+def test_fp32_o_entries_validation():
+    L = lib()
+    # attn_fwd_o32(q, k, v, o, o32, lse, ties, pone, formed, B, H, N, D, scale, causal, stab, beta, stream)
+    base = [addr(0), addr(1), addr(2), addr(3), addr(4), addr(5), None, None, None, 1, 2, 64, 64, 0.125, 1, 1, 2.0,
+            None]
+    bad = list(base)
+    bad[4] = None
+    assert L.attn_fwd_o32(*bad) == -1          # o32 is required here
+    bad = list(base)
+    bad[4] = addr(4) + 4
+    assert L.attn_fwd_o32(*bad) == -6
+    bad = list(base)
+    bad[4] = addr(2) + 64
+    assert L.attn_fwd_o32(*bad) == -7          # o32 inside v
+    bad = list(base)
+    bad[15] = 5
+    assert L.attn_fwd_o32(*bad) == -10
+    bad = list(base)
+    bad[5] = addr(4) + 4096
+    assert L.attn_fwd_o32(*bad) == -7          # lse inside o32 (fp32: twice the bf16 bytes)
+    # attn_bwd_o32(q, k, v, o32, dO, lse, dq, dk, dv, delta, B, H, N, D, scale, causal, stab, beta, stream)
+    b = [addr(i) for i in range(10)] + [1, 2, 64, 64, 0.125, 1, 1, 2.0, None]
+    bad = list(b)
+    bad[3] = None
+    assert L.attn_bwd_o32(*bad) == -1
+    bad = list(b)
+    bad[6] = addr(3) + 16
+    assert L.attn_bwd_o32(*bad) == -7          # dq inside o32
+    bad = list(b)
+    bad[13] = 80
+    assert L.attn_bwd_o32(*bad) == -3
+    assert L.attn_bwd_o32(*(b[:10] + [0] + b[11:])) == 0   # empty problem

@@ -23,6 +23,17 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
+def nss_forward_o32(t, w):
+    import numerics_safe_softmax_amd as nss
+    return nss.forward(t["q"], t["k"], t["v"], scale=w.scale, causal=w.causal, stabilise=0, beta=w.beta, o32=True)
+
+
+def nss_backward_o32(t, w, f):
+    import numerics_safe_softmax_amd as nss
+    return nss.backward(t["q"], t["k"], t["v"], f["o"], t["dO"], f["lse"], scale=w.scale, causal=w.causal,
+                        o32=f["o32"])
+
+
 CASES = [("tiny", [0]), ("gpt2_small", list(range(0, 96, 8))), ("sink", [0, 17, 33]),
          ("gpt2_medium", [3, 64, 120])]
 REPORT = {}
@@ -70,6 +81,21 @@ def test_events_and_bias(wname, heads):
             exn = exact & (ref["amb_near"] == 0)
             assert np.array_equal(formed[2][exn], ref["near_ones"][exn])
         res[{0: "unstabilised", 1: "stabilised", 2: "stabilised_exact"}[stabilise]] = rep
+    # the high-precision delta path (delta from the forward's fp32 O), plain forward
+    f = nss_forward_o32(t, w)
+    b = nss_backward_o32(t, w, f)
+    torch.cuda.synchronize()
+    ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=False,
+                         beta=w.beta, rows=rows, want=parity.FWD_WANT)
+    rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=w.causal, heads=heads)
+    O = parity.f64(f["o"])
+    O_round = inputs.bits_to_float(oracle.bf16_from_double(np.nan_to_num(ref["O"]), "rne")).astype(np.float64)
+    rep = bias.report(O, ref["O"], parity.f64(b["delta"]), rb["delta"],
+                      inputs.bits_to_float(d["dO"]).astype(np.float64), ref["ties"], rmask,
+                      w.v_skew_dims, O_ref_rounded=O_round)
+    res["unstabilised_fp32_o_delta"] = rep
+    print("  delta bias z on tie rows: bf16-O delta %.2f, fp32-O delta %.2f" % (
+        res["unstabilised"]["delta_tie_rows"]["z"], rep["delta_tie_rows"]["z"]), flush=True)
     # both stabilised shifts are never below the plain kernel's running max at any
     # tile (online: same running max sequence; exact: the final max), so neither
     # forms more bf16 ones than the plain kernel on any row

@@ -156,3 +156,32 @@ def test_workload_parity(wname, heads):
         if stabilise == 2:
             okn = rmask & (ref["amb_tie"] == 0) & (ref["amb_near"] == 0)
             assert np.array_equal(f["formed_ones"].cpu().numpy()[okn], ref["near_ones"][okn])
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", SMALL[:5] + SMALL[6:7], ids=lambda c: "B%dH%dN%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
+def test_fp32_o_path(case, mode):
+    """attn_fwd_o32 / attn_bwd_o32: the bf16 O is the nearest-even rounding of
+    the fp32 O, the rest of the forward equals attn_fwd bit for bit, and delta
+    taken from the fp32 O (and the gradients after it) match the oracle."""
+    import numerics_safe_softmax_amd as nss
+    w = _small_workload(*case)
+    _say("fp32-O path %s mode=%d" % (case, mode))
+    d = inputs.generate(w)
+    t = parity.to_dev(d, DEV)
+    f = nss.forward(t["q"], t["k"], t["v"], scale=w.scale, causal=w.causal, stabilise=mode, beta=w.beta, o32=True)
+    f0 = parity.gpu_forward(t, w, mode)
+    b = nss.backward(t["q"], t["k"], t["v"], f["o"], t["dO"], f["lse"], scale=w.scale, causal=w.causal,
+                     stabilise=mode, beta=w.beta, o32=f["o32"])
+    torch.cuda.synchronize()
+    assert torch.equal(f["o32"].to(torch.bfloat16).view(torch.int16), f["o"].view(torch.int16))
+    for key in ("o", "lse", "ties", "pbar_one", "formed_ones"):
+        a, c = f[key], f0[key]
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           c.view(torch.int16) if c.dtype == torch.bfloat16 else c), key
+    ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=mode != 0, beta=w.beta)
+    rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=w.causal)
+    r32 = parity.ratio(f["o32"].double().cpu().numpy(), ref["O"], ref["tol_O"])
+    assert r32 <= 1.0
+    br = parity.check_backward(b, rb, label="o32 " + str(case))
+    _say("  O32 err/tol %.3f, bwd %s" % (r32, br))
