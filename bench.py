@@ -358,11 +358,41 @@ def cpu_leg(w, d, nss, t, stream):
         rep["pbar_one_events_on_tie_rows"] = int(f["pbar_one"].cpu().numpy()[ref["ties"] > 1].sum())
         rep["formed_ones_on_tie_rows"] = int(f["formed_ones"].cpu().numpy()[ref["ties"] > 1].sum())
         res[names[stabilise]] = rep
+    res["bf16_accumulation_emulation"] = emulation_curves()
     res["O_mode_difference_z"] = bias.mode_difference(
         res["stabilised_exact"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"],
         res["unstabilised"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"])
     res["tie_rows"] = int((ref["ties"] > 1).sum())
     return cpu, res
+
+
+def emulation_curves():
+    """The pages' mechanism on the CPU (oracle.emulate_bf16_pv): P_bar V with
+    every product and addition rounded to bf16, nearest-even vs ties-away,
+    plain vs shifted; signed O error (bf16 ulps of the exact O, skewed V dims)
+    grouped by the row's count of P_bar entries equal to 1.  Bounded sample:
+    the tiny workload (all rows) and two heads of gpt2_small."""
+    import numpy as np
+
+    import oracle
+    from oracle import bias
+    from numerics_safe_softmax_amd import inputs
+    out = {}
+    t0 = time.perf_counter()
+    for wname, heads in (("tiny", [0]), ("gpt2_small", [0, 1])):
+        w = inputs.WORKLOADS[wname]
+        d = inputs.generate(w)
+        rows = oracle.head_rows(heads, w.N)
+        ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, rows=rows, want=["O"])
+        mask = ~np.isnan(ref["O"][..., 0])
+        for stab in (False, True):
+            for mode in ("rne", "rna"):
+                r = oracle.emulate_bf16_pv(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=stab,
+                                           beta=w.beta, accumulate=mode, rows=rows)
+                out["%s/%s/%s" % (wname, "shift" if stab else "plain", mode)] = bias.event_curve(
+                    r["O"], ref["O"], r["events"], mask, w.v_skew_dims)
+    out["seconds"] = time.perf_counter() - t0
+    return out
 
 
 def inputs_f64(bits):

@@ -93,6 +93,8 @@ def lib():
         L.orc_backward.restype = ctypes.c_int
         L.orc_backward.argtypes = [ctypes.POINTER(_Problem), _P, ctypes.c_int64, _P, _P, _P, _P,
                                    ctypes.POINTER(_BwdOut)]
+        L.orc_emulate_pv.restype = ctypes.c_int
+        L.orc_emulate_pv.argtypes = [ctypes.POINTER(_Problem), _P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P, _P]
         L.orc_threads.restype = ctypes.c_int
         L.orc_threads.argtypes = []
         _lib = L
@@ -222,6 +224,29 @@ def backward(q, k, v, dO, fwd: dict, *, scale: float, causal: bool,
     if rc != 0:
         raise ValueError("oracle backward rejected the inputs")
     return res
+
+
+def emulate_bf16_pv(q, k, v, *, scale: float, causal: bool, stabilise: bool = False, beta: float = 2.0,
+                    accumulate: str = "rne", round_pbar: bool = True,
+                    rows: Optional[Sequence[int]] = None) -> dict:
+    """P_bar V accumulated in bf16, one rounding per product and per addition
+    (see ``emulate_row`` in oracle.c), normalised by the FP64 row sum.
+
+    accumulate: a rounding mode ("rne", "rna", "rtz", "rd", "ru") or "exact"
+    (FP64 accumulation of the exact products).  Returns {"O": [B, H, N, D]
+    float64, "events": [B, H, N] int32 = P_bar entries equal to 1}; rows not
+    computed are NaN / -1.
+    """
+    p, keep, (B, H, N, D) = _problem(q, k, v, None, scale, causal, stabilise, beta)
+    O = np.full((B, H, N, D), np.nan)
+    ev = np.full((B, H, N), -1, dtype=np.int32)
+    rr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    mode = -1 if accumulate == "exact" else MODES[accumulate]
+    rc = lib().orc_emulate_pv(ctypes.byref(p), _ptr(rr), 0 if rr is None else rr.size, int(bool(round_pbar)),
+                              mode, _ptr(O), _ptr(ev))
+    if rc != 0:
+        raise ValueError("oracle emulation rejected the inputs")
+    return {"O": O, "events": ev}
 
 
 def head_rows(heads: Sequence[int], N: int) -> np.ndarray:

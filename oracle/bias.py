@@ -105,3 +105,21 @@ def report(O_gpu, O_ref, delta_gpu, delta_ref, dO, ties, rows_mask, skew_dims: i
             "delta_single_max_rows": delta_bias(delta_gpu, d_round, dO, O_ref, notie),
         }
     return out
+
+
+def event_curve(O_emul, O_exact, events, rows_mask, skew_dims: int) -> dict:
+    """Signed error of an emulated O against the exact one, in bf16 ulps of the
+    exact value, on the skewed V dims, grouped by how many P_bar entries of
+    the row equal 1 (the trigger of the pages' mechanism).  Per group: rows,
+    mean, row-clustered SEM and z."""
+    skew = np.arange(skew_dims)
+    out = {}
+    for lo, hi, name in ((0, 0, "0"), (1, 1, "1"), (2, 2, "2"), (3, 3, "3"), (4, 1 << 30, ">=4")):
+        m = rows_mask & (events >= lo) & (events <= hi)
+        if not m.any():
+            continue
+        e = (O_emul[..., skew] - O_exact[..., skew]) / ulp_bf16(O_exact[..., skew])
+        st = _stats(e[m].mean(axis=-1))
+        st["rows"] = st.pop("n_rows") if "n_rows" in st else int(m.sum())
+        out[name] = st
+    return out

@@ -558,6 +558,82 @@ int orc_forward(const orc_problem* p, const int64_t* rows, int64_t nrows, const 
 }
 
 /* ------------------------------------------------------------------ */
+/* emulation of a bf16-accumulated P_bar V                             */
+/* ------------------------------------------------------------------ */
+
+/*
+ * [ITS] section "机制解释二" and [HM] section 四: with several P_bar entries
+ * exactly 1 (a repeated row max) the products P_bar V are the V values
+ * themselves, and adding mostly negative bf16 numbers in bf16 (significand
+ * overflow, a right shift, the shifted-out and sticky bits deciding the
+ * rounding) errs to one side.  This emulates that arithmetic for one row,
+ * in key order:
+ *   P_bar_j = exp(S_j - m*) (FP64, m* from the duplicate-max rule when
+ *             p->stabilise), rounded to bf16 nearest-even when pbar_round;
+ *   term_j  = P_bar_j * v_jc, exact, then rounded to bf16 in acc_mode;
+ *   acc     = acc (+) term_j, the exact sum rounded to bf16 in acc_mode;
+ *   O_c     = acc / l, l = sum_j P_bar_j in FP64.
+ * acc_mode < 0 accumulates the exact terms in FP64 instead (no bf16 step).
+ * events = how many P_bar_j equal 1 after the rounding.
+ */
+static void emulate_row(const orc_problem* p, const decoded* dc, int64_t row, row_scratch* s, int pbar_round,
+                        int acc_mode, double* O, int32_t* events) {
+  const int N = p->N, D = p->D;
+  const int64_t bh = row / N;
+  const int i = (int)(row % N);
+  const int jl = last_key(p, i);
+  double rm_raw;
+  int rs;
+  row_scores(p, dc, bh, i, jl, s, &rm_raw, &rs);
+  const double m = orc_shift_rule(p->scale * rm_raw, rs, p->stabilise, p->beta);
+  double* pb = s->sabs;  /* reuse: P_bar per key */
+  double l = 0.0;
+  int ev = 0;
+  for (int j = 0; j <= jl; ++j) {
+    double x = exp(p->scale * s->raw[j] - m);
+    if (pbar_round) x = orc_bf16_decode(orc_bf16_from_double(x, ORC_RNE));
+    pb[j] = x;
+    l += x;
+    if (x == 1.0) ++ev;
+  }
+  for (int c = 0; c < D; ++c) {
+    if (acc_mode < 0) {
+      double acc = 0.0;
+      for (int j = 0; j <= jl; ++j) acc += pb[j] * dc->v[(bh * N + j) * D + c];
+      O[row * D + c] = acc / l;
+    } else {
+      uint16_t acc = 0;
+      for (int j = 0; j <= jl; ++j) {
+        const uint16_t term = orc_bf16_from_double(pb[j] * dc->v[(bh * N + j) * D + c], acc_mode);
+        acc = orc_bf16_add(acc, term, acc_mode);
+      }
+      O[row * D + c] = orc_bf16_decode(acc) / l;
+    }
+  }
+  if (events) events[row] = ev;
+}
+
+/* rows: flattened row indices or NULL for all; O [B][H][N][D], events [B][H][N] (nullable). */
+int orc_emulate_pv(const orc_problem* p, const int64_t* rows, int64_t nrows, int pbar_round, int acc_mode,
+                   double* O, int32_t* events) {
+  if (p->N <= 0 || p->B <= 0 || p->H <= 0) return 0;
+  if (!p->v) return -1;
+  decoded dc;
+  if (decode_problem(p, &dc) != 0) { free_decoded(&dc); return -1; }
+  const int64_t total = rows ? nrows : (int64_t)p->B * p->H * p->N;
+#pragma omp parallel
+  {
+    row_scratch s;
+    scratch_init(&s, p->N);
+#pragma omp for schedule(dynamic, 8)
+    for (int64_t t = 0; t < total; ++t) emulate_row(p, &dc, rows ? rows[t] : t, &s, pbar_round, acc_mode, O, events);
+    scratch_free(&s);
+  }
+  free_decoded(&dc);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* backward                                                            */
 /* ------------------------------------------------------------------ */
 
