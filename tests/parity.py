@@ -32,8 +32,11 @@ def gpu_backward(t, w, f, stabilise):
 
 
 def ratio(got, want, tol, mask=None):
-    """Largest |got - want| / tol over the (optionally masked) elements."""
-    r = np.abs(got - want) / tol
+    """Largest |got - want| / tol over the (optionally masked) elements; where
+    the tolerance is 0 (e.g. dK = 0 exactly when Q = 0) only equality passes."""
+    err = np.abs(got - want)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(tol > 0, err / np.where(tol > 0, tol, 1.0), np.where(err == 0, 0.0, np.inf))
     if mask is not None:
         r = r[mask]
     return float(np.max(r)) if r.size else 0.0

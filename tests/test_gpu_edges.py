@@ -1,0 +1,118 @@
+"""Degenerate and extreme cases of the method on the GPU, against the oracle.
+
+* Q = 0: every score is 0, so every visible key ties at rm = 0; the rule's
+  strict comparisons fall through to m = rm (itsolotime.com/archives/23922,
+  section 极简修复方案), P_bar = 1 everywhere and pbar_one = 1 even when
+  stabilising; O is the running mean of V and LSE = ln(visible keys).
+* A repeated maximum that is negative: the rule shifts by 0, so the largest
+  P_bar is exp(rm) < 1 and pbar_one = 0.
+* A long sequence (N = 32768, d = 128): forward parity on sampled rows, in the
+  launch configuration of any other call (64-bit offsets, many KV tiles).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from numerics_safe_softmax_amd import inputs
+from tests import parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bits(x):
+    return inputs.to_bf16_bits(np.asarray(x, dtype=np.float64))
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("D", [64, 128])
+def test_zero_queries_tie_at_zero(mode, D):
+    import numerics_safe_softmax_amd as nss
+    rng = np.random.default_rng(40 + D)
+    B, H, N = 1, 2, 300
+    q = _bits(np.zeros((B, H, N, D)))
+    k = _bits(rng.standard_normal((B, H, N, D)))
+    v = _bits(rng.standard_normal((B, H, N, D)))
+    dO = _bits(rng.standard_normal((B, H, N, D)))
+    t = {n: inputs.to_torch(x, DEV) for n, x in (("q", q), ("k", k), ("v", v), ("dO", dO))}
+    f = nss.forward(t["q"], t["k"], t["v"], scale=D ** -0.5, causal=True, stabilise=mode, beta=2.0)
+    b = nss.backward(t["q"], t["k"], t["v"], f["o"], t["dO"], f["lse"], scale=D ** -0.5, causal=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(q, k, v, scale=D ** -0.5, causal=True, stabilise=mode != 0, beta=2.0)
+    rb = oracle.backward(q, k, v, dO, ref, scale=D ** -0.5, causal=True)
+    fr = parity.check_forward(f, ref, label="Q=0 D%d mode %d" % (D, mode))
+    br = parity.check_backward(b, rb, label="Q=0")
+    visible = np.arange(1, N + 1)
+    assert np.array_equal(f["ties"].cpu().numpy()[0, 0], visible)
+    assert np.all(f["pbar_one"].cpu().numpy() == 1)          # rm == 0: the rule does not fire
+    assert np.all(ref["flags"][..., 1:] & 1)                 # the oracle flags every tied row (R4)
+    assert not np.any(ref["flags"][..., 0] & 1)              # row 0 sees one key: no tie
+    lse = f["lse"].cpu().numpy()[0, 0].astype(np.float64)
+    assert np.allclose(lse, np.log(visible), rtol=0, atol=1e-5)
+    _say("  Q=0 D%d mode %d fwd %s bwd %s" % (D, mode, fr, br))
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_negative_repeated_maximum(mode):
+    """Keys point away from the queries (all scores negative); the argmax key
+    of each row is duplicated at an earlier position."""
+    import numerics_safe_softmax_amd as nss
+    rng = np.random.default_rng(77)
+    B, H, N, D = 1, 1, 256, 64
+    base = rng.standard_normal(D)
+    qf = base + 0.1 * rng.standard_normal((B, H, N, D))
+    kf = -base - 0.3 * rng.standard_normal((B, H, N, D))
+    q, k = _bits(qf), _bits(kf)
+    qd, kd = inputs.bits_to_float(q).astype(np.float64), inputs.bits_to_float(k).astype(np.float64)
+    for i in range(8, N, 7):                     # copy row i's best key to an earlier slot
+        s = kd[0, 0, :i + 1] @ qd[0, 0, i]
+        j = int(np.argmax(s))
+        slot = (j + 3) % i if (j + 3) % i != j else (j + 1) % i
+        k[0, 0, slot] = k[0, 0, j]
+        kd[0, 0, slot] = kd[0, 0, j]
+    v = _bits(rng.standard_normal((B, H, N, D)))
+    dO = _bits(rng.standard_normal((B, H, N, D)))
+    t = {n: inputs.to_torch(x, DEV) for n, x in (("q", q), ("k", k), ("v", v), ("dO", dO))}
+    f = nss.forward(t["q"], t["k"], t["v"], scale=0.125, causal=True, stabilise=mode, beta=2.0)
+    b = nss.backward(t["q"], t["k"], t["v"], f["o"], t["dO"], f["lse"], scale=0.125, causal=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(q, k, v, scale=0.125, causal=True, stabilise=mode != 0, beta=2.0)
+    rb = oracle.backward(q, k, v, dO, ref, scale=0.125, causal=True)
+    parity.check_forward(f, ref, label="negative max mode %d" % mode)
+    parity.check_backward(b, rb, label="negative max")
+    neg_tie = (ref["ties"] > 1) & (ref["rowmax"] < 0) & (ref["amb_tie"] == 0) & (ref["amb_pbar"] == 0)
+    assert neg_tie.sum() > 20
+    pone = f["pbar_one"].cpu().numpy()
+    if mode:
+        assert np.all(pone[neg_tie] == 0)
+    else:
+        assert np.all(pone[neg_tie] == 1)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_long_sequence_sampled_rows(mode):
+    import numerics_safe_softmax_amd as nss
+    w = inputs.custom("long", 1, 2, 32768, 128, True, 91, tie_block=50, v_skew_dims=64, v_mu=-1.5, v_sigma=0.5)
+    _say("long sequence N=32768 mode %d" % mode)
+    d = inputs.generate(w)
+    t = parity.to_dev(d, DEV)
+    f = nss.forward(t["q"], t["k"], t["v"], scale=w.scale, causal=True, stabilise=mode, beta=w.beta)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.sort(np.concatenate([rng.choice(w.N, 24, replace=False), [0, 1, 127, 128, w.N - 1],
+                                   w.N + rng.choice(w.N, 24, replace=False)]))
+    ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=True, stabilise=mode != 0, beta=w.beta,
+                         rows=rows, want=parity.FWD_WANT)
+    m = np.zeros((1, 2, w.N), dtype=bool)
+    m.reshape(-1)[rows] = True
+    fr = parity.check_forward(f, ref, rows_mask=m, label="long mode %d" % mode)
+    _say("  %s" % fr)
