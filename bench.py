@@ -39,8 +39,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2_small.md")
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # the GPU needs tens of milliseconds of load to reach its working clock:
+    # 300 warm-up steps (~35 ms) before 500 timed ones (~55 ms)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--workload", default="gpt2_small")
     p.add_argument("--mode", type=int, default=1, choices=(1, 2),
                    help="stabilised forward: 1 = online shift, 2 = exact final shift (two passes)")
