@@ -55,6 +55,11 @@
 #ifndef NSS_FWD_STAGES
 #define NSS_FWD_STAGES 2
 #endif
+// LDS swizzle of the forward kernels' K/V tiles (see Tile): 0 keeps them at
+// three waves per SIMD for D = 64
+#ifndef NSS_FWD_SWZ
+#define NSS_FWD_SWZ 0
+#endif
 
 namespace nss {
 
@@ -69,11 +74,17 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+constexpr int kFwdSW = NSS_FWD_SWZ;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // bf16 rounds x to exactly 1.0 (nearest even) iff 1 - 2^-9 <= x <= 1 + 2^-8;
 // every P_bar here is at most 1 (plus exp2 rounding), so one compare decides.
 constexpr float kBf16OneLow = 0.998046875f;
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -98,12 +109,17 @@ __device__ __forceinline__ void wait_vmem_le() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// eight fp32 accumulator values -> the bf16 B operand of the next contraction
-__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
+// eight fp32 accumulator values -> the bf16 B operand of the next contraction.
+// k-slice m (0 or 1) takes elements 4m..4m+3 and 8+4m..8+4m+3, i.e. score
+// rows 8m + 4h + {0..3} and 16 + 8m + 4h + {0..3}: the two row quads of one
+// k-slice are 16 rows apart, so the transposed LDS reads of the other operand
+// (Tile::trans8) sit at a constant offset from each other.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int m) {
   bf16x8 r;
 #pragma unroll
   for (int t = 0; t < 8; t += 2) {
-    bf16x2 p = __builtin_convertvector(f32x2{s[base + t], s[base + t + 1]}, bf16x2);
+    const int e = (t < 4 ? 4 * m : 8 + 4 * m) + (t & 3);
+    bf16x2 p = __builtin_convertvector(f32x2{s[e], s[e + 1]}, bf16x2);
     r[t] = p[0];
     r[t + 1] = p[1];
   }
@@ -112,16 +128,33 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
 
 // ---------------------------------------------------------------------------
 // LDS tiles: R rows x D bf16, row-major, rows of D/8 16-byte chunks; chunk c
-// of row r sits at chunk c ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1).  The
-// eight rows one ds_read_b128 phase touches get eight different f (distinct
-// banks), and the four rows a ds_read_b64_tr_b16 group reads (32 bytes each,
-// an even/odd chunk pair) get pairs f = b, 2+b, 4+b, 6+b, whose chunk pairs
-// are disjoint (no bank conflict on 32 banks either).
+// of row r sits at chunk c ^ f(r).  The LDS serves 64 four-byte banks (256
+// bytes) per cycle; a ds_read_b128 of 64 lanes runs in 16-lane phases, and in
+// the row-operand reads (lane l: row l % 32, one chunk) a phase covers 16
+// consecutive rows.  f is chosen so those 16 rows fall on distinct banks:
+//   D = 64 (two rows per 256 bytes): f = r2 | (r2 ^ r3) << 1 | r1 << 2 is a
+//     bijection of (r1, r2, r3), so the eight rows of one parity differ;
+//   D = 128 (one row per 256 bytes): f = r2 | (r1 ^ r3) << 1 | r1 << 2 | r0 << 3
+//     is a bijection of r mod 16.
+// The transposed reads (32 lanes: 4 consecutive rows x 4 chunks) are
+// conflict-free too: for D = 64 rows r and r + 2 differ in bit 2 of f, for
+// D = 128 rows r .. r + 3 differ in bits 2-3.  f depends on r mod 16 only, so
+// the rows r and r + 16 one trans8 call reads share an address pattern.
+// Because f depends on r3, the two k-slices of a 32-row block (8 rows apart)
+// need separate LDS addresses; SW = 0 selects the older f = r2 | r0 << 1 |
+// r1 << 2 (distinct banks within 8 rows only: the 16-lane row reads take two
+// passes) that keeps every trans8 read at a constant offset, for a kernel
+// that cannot spare the registers.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int SW = 1>
 struct Tile {
   static constexpr int CPR = D / 8;
-  __device__ static __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+  __device__ static __forceinline__ int swz(int r) {
+    const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+    if constexpr (SW == 0) return r2 | (r0 << 1) | (r1 << 2);
+    else if constexpr (D == 64) return r2 | ((r2 ^ r3) << 1) | (r1 << 2);
+    else return r2 | ((r1 ^ r3) << 1) | (r1 << 2) | (r0 << 3);
+  }
   __device__ static __forceinline__ int chunk(int r, int c) { return r * CPR + (c ^ swz(r)); }
   // 8 bf16 of row r starting at column 8c (an MFMA A/B row operand)
   __device__ static __forceinline__ bf16x8 row8(const uint16_t* t, int r, int c) {
@@ -133,14 +166,15 @@ struct Tile {
     s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
     return __builtin_bit_cast(u32x2, v);
   }
-  // A operand of X^T (rows = columns of the tile, k = tile rows): for lane l,
-  // column 32*cb + l%32, tile rows r0 + 4h + {0..3} and r0 + 8 + 4h + {0..3}.
-  __device__ static __forceinline__ bf16x8 trans8(const uint16_t* t, int r0, int cb, int lane) {
+  // A operand of X^T for k-slice m of the 32 tile rows from r0 (the pairing of
+  // pack8): for lane l, column 32*cb + l%32, tile rows r0 + 8m + 4h + {0..3}
+  // and r0 + 16 + 8m + 4h + {0..3}.
+  __device__ static __forceinline__ bf16x8 trans8(const uint16_t* t, int r0, int m, int cb, int lane) {
     const int L = lane & 15, h = lane >> 5, G = (lane >> 4) & 1;
-    const int r = r0 + 4 * h + (L >> 2);
+    const int r = r0 + 8 * m + 4 * h + (L >> 2);
     const int col = 32 * cb + 16 * G + 4 * (L & 3);
     const u32x2 a = tr4(t, r, col);
-    const u32x2 b = tr4(t, r + 8, col);
+    const u32x2 b = tr4(t, r + 16, col);
     return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
   }
 };
@@ -148,7 +182,7 @@ struct Tile {
 // Rows [r0, r0+R) of a bf16 [N][D] matrix straight into a swizzled LDS tile;
 // every thread of the 256 issues (R*D/8)/256 16-byte loads.  Rows past N read
 // row N-1 (finite data; the kernels mask them).
-template <int R, int D>
+template <int R, int D, int SW = 1>
 __device__ __forceinline__ void tile_to_lds(const uint16_t* __restrict__ src, int r0, int N, uint16_t* tile,
                                             int wu, int lane) {
   constexpr int CPR = D / 8, TOT = R * CPR, PER = TOT / 256;
@@ -157,7 +191,7 @@ __device__ __forceinline__ void tile_to_lds(const uint16_t* __restrict__ src, in
   for (int i = 0; i < PER; ++i) {
     const int P = i * 256 + wu * 64 + lane;
     const int r = P / CPR, p = P % CPR;
-    const int c = p ^ Tile<D>::swz(r);
+    const int c = p ^ Tile<D, SW>::swz(r);
     int gr = r0 + r;
     gr = gr < N ? gr : N - 1;
     __builtin_amdgcn_global_load_lds(src + (size_t)gr * D + c * 8, (lds_void*)(tile + (i * 256 + wu * 64) * 8), 16,
@@ -237,8 +271,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   const int nkt = (kend + BN - 1) / BN;
   auto fetch = [&](int kt, int buf) {
     uint16_t* base = lds + buf * NT * TILE;
-    tile_to_lds<BN, D>(K + head, kt * BN, N, base, wu, lane);
-    if constexpr (!TIES_ONLY) tile_to_lds<BN, D>(V + head, kt * BN, N, base + TILE, wu, lane);
+    tile_to_lds<BN, D, kFwdSW>(K + head, kt * BN, N, base, wu, lane);
+    if constexpr (!TIES_ONLY) tile_to_lds<BN, D, kFwdSW>(V + head, kt * BN, N, base + TILE, wu, lane);
   };
   bf16x8 qf[NKK];
 #pragma unroll
@@ -275,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = Tile<D>::row8(Kt, 32 * kb + li, 2 * kk + h);
+      for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = Tile<D, kFwdSW>::row8(Kt, 32 * kb + li, 2 * kk + h);
     f32x16 s[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
@@ -290,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) va[kb][m][cb] = Tile<D>::trans8(Vt, 32 * kb + 16 * m, cb, lane);
+          for (int cb = 0; cb < NCB; ++cb) va[kb][m][cb] = Tile<D, kFwdSW>::trans8(Vt, 32 * kb, m, cb, lane);
     }
     if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
 #pragma unroll
@@ -345,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 p0 = pack8(s[kb], 0), p1 = pack8(s[kb], 8);
+        const bf16x8 p0 = pack8(s[kb], 0), p1 = pack8(s[kb], 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           oacc[cb] = mfma(va[kb][0][cb], p0, oacc[cb]);
@@ -436,8 +470,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
   const int nkt = (kend + BN - 1) / BN;
   auto fetch = [&](int kt, int buf) {
     uint16_t* base = lds + buf * 2 * TILE;
-    tile_to_lds<BN, D>(K + head, kt * BN, N, base, wu, lane);
-    tile_to_lds<BN, D>(V + head, kt * BN, N, base + TILE, wu, lane);
+    tile_to_lds<BN, D, kFwdSW>(K + head, kt * BN, N, base, wu, lane);
+    tile_to_lds<BN, D, kFwdSW>(V + head, kt * BN, N, base + TILE, wu, lane);
   };
   bf16x8 qf[NKK];
 #pragma unroll
@@ -469,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = Tile<D>::row8(Kt, 32 * kb + li, 2 * kk + h);
+      for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = Tile<D, kFwdSW>::row8(Kt, 32 * kb + li, 2 * kk + h);
     f32x16 s[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
@@ -483,7 +517,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) va[kb][m][cb] = Tile<D>::trans8(Vt, 32 * kb + 16 * m, cb, lane);
+        for (int cb = 0; cb < NCB; ++cb) va[kb][m][cb] = Tile<D, kFwdSW>::trans8(Vt, 32 * kb, m, cb, lane);
     if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -509,7 +543,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const bf16x8 p0 = pack8(s[kb], 0), p1 = pack8(s[kb], 8);
+      const bf16x8 p0 = pack8(s[kb], 0), p1 = pack8(s[kb], 1);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         oacc[cb] = mfma(va[kb][0][cb], p0, oacc[cb]);
@@ -605,8 +639,16 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) dqa[cb] = f32x16{};
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
+  // dP accumulates onto -delta (one value per query, i.e. per lane), so
+  // dP - delta comes out of the products
+  f32x16 negd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = -dl;
+
+  // one key tile; the LDS buffer is a compile-time constant so that every LDS
+  // address is a loop-invariant register plus an immediate offset
+  auto tile = [&](const int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     wait_vmem();
     __syncthreads();
     if (kt + 1 < nkt) fetch(kt + 1, buf ^ 1);
@@ -614,13 +656,13 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
     const uint16_t* Vt = Kt + TILE;
     const int k0 = kt * BN;
     const bool active = qw < N && (!CAUSAL || k0 <= qw + 31);
-    if (!active) continue;
+    if (!active) return;
 
-    // one 32-key block at a time: S, dP, dS, then dQ (halves the live
-    // score registers)
+    // one 32-key block at a time: S, dP, dS, then dQ (halves the live score
+    // registers)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      f32x16 s = f32x16{}, dp = negd;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         s = mfma(Tile<D>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s);
@@ -636,15 +678,19 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = exp2f_fast(__builtin_fmaf(s[r], t, -lse2));
-        s[r] = p * (dp[r] - dl);
+        s[r] = p * dp[r];
       }
-      const bf16x8 d0 = pack8(s, 0), d1 = pack8(s, 8);
+      const bf16x8 d0 = pack8(s, 0), d1 = pack8(s, 1);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        dqa[cb] = mfma(Tile<D>::trans8(Kt, 32 * kb, cb, lane), d0, dqa[cb]);
-        dqa[cb] = mfma(Tile<D>::trans8(Kt, 32 * kb + 16, cb, lane), d1, dqa[cb]);
+        dqa[cb] = mfma(Tile<D>::trans8(Kt, 32 * kb, 0, cb, lane), d0, dqa[cb]);
+        dqa[cb] = mfma(Tile<D>::trans8(Kt, 32 * kb, 1, cb, lane), d1, dqa[cb]);
       }
     }
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    tile(kt, IntC<0>{});
+    if (kt + 1 < nkt) tile(kt + 1, IntC<1>{});
   }
 
   if (qi >= N) return;
@@ -699,7 +745,7 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_ke
   auto commit_rows = [&](int buf) {
     if (tid < BQ) {
       rowv[buf][0][tid] = rl;
-      rowv[buf][1][tid] = rd;
+      rowv[buf][1][tid] = -rd;  // -delta: the initial value of the dP accumulator
     }
   };
   fetch(qstart, 0);
@@ -721,8 +767,10 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_ke
   wait_vmem();
   commit_rows(0);
 
-  for (int qt = qstart; qt < nqt; ++qt) {
-    const int buf = (qt - qstart) & 1;
+  // one query tile; the LDS buffer is a compile-time constant so that every
+  // LDS address is a loop-invariant register plus an immediate offset
+  auto tile = [&](const int qt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     wait_vmem();
     __syncthreads();
     if (qt + 1 < nqt) fetch(qt + 1, buf ^ 1);
@@ -735,7 +783,14 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_ke
       // the live score registers)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+        // dP accumulates onto -delta, so dP - delta comes out of the products
+        f32x16 s = f32x16{}, dp;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&rowv[buf][1][32 * qb + 8 * g + 4 * h]);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) dp[4 * g + jj] = d4[jj];
+        }
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
           s = mfma(Tile<D>::row8(Qt, 32 * qb + li, 2 * kk + h), kf[kk], s);
@@ -750,25 +805,23 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_ke
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int rr = 32 * qb + 8 * g + 4 * h;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&rowv[buf][0][rr]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&rowv[buf][1][rr]);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&rowv[buf][0][32 * qb + 8 * g + 4 * h]);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int r = 4 * g + jj;
             const float p = exp2f_fast(__builtin_fmaf(s[r], t, -l4[jj]));
             s[r] = p;
-            dp[r] = p * (dp[r] - d4[jj]);
+            dp[r] = p * dp[r];
           }
         }
-        const bf16x8 p0 = pack8(s, 0), p1 = pack8(s, 8);
-        const bf16x8 d0 = pack8(dp, 0), d1 = pack8(dp, 8);
+        const bf16x8 p0 = pack8(s, 0), p1 = pack8(s, 1);
+        const bf16x8 d0 = pack8(dp, 0), d1 = pack8(dp, 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          dva[cb] = mfma(Tile<D>::trans8(Gt, 32 * qb, cb, lane), p0, dva[cb]);
-          dva[cb] = mfma(Tile<D>::trans8(Gt, 32 * qb + 16, cb, lane), p1, dva[cb]);
-          dka[cb] = mfma(Tile<D>::trans8(Qt, 32 * qb, cb, lane), d0, dka[cb]);
-          dka[cb] = mfma(Tile<D>::trans8(Qt, 32 * qb + 16, cb, lane), d1, dka[cb]);
+          dva[cb] = mfma(Tile<D>::trans8(Gt, 32 * qb, 0, cb, lane), p0, dva[cb]);
+          dva[cb] = mfma(Tile<D>::trans8(Gt, 32 * qb, 1, cb, lane), p1, dva[cb]);
+          dka[cb] = mfma(Tile<D>::trans8(Qt, 32 * qb, 0, cb, lane), d0, dka[cb]);
+          dka[cb] = mfma(Tile<D>::trans8(Qt, 32 * qb, 1, cb, lane), d1, dka[cb]);
         }
       }
     }
@@ -776,6 +829,10 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_ke
       wait_vmem();
       commit_rows(buf ^ 1);
     }
+  };
+  for (int qt = qstart; qt < nqt; qt += 2) {
+    tile(qt, IntC<0>{});
+    if (qt + 1 < nqt) tile(qt + 1, IntC<1>{});
   }
 
   if (kj >= N) return;
