@@ -146,23 +146,18 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # per-kernel HIP events on the launch stream (separate pass of K steps)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        fwd()
-        ev[s][1].record(stream)
-        bwd_dq()
-        ev[s][2].record(stream)
-        bwd_dkdv()
-        ev[s][3].record(stream)
-    torch.cuda.synchronize()
-    per = {"fwd": [], "bwd_dq": [], "bwd_dkdv": []}
-    for s in range(args.steps):
-        per["fwd"].append(ev[s][0].elapsed_time(ev[s][1]))
-        per["bwd_dq"].append(ev[s][1].elapsed_time(ev[s][2]))
-        per["bwd_dkdv"].append(ev[s][2].elapsed_time(ev[s][3]))
-    us = {k2: float(np.mean(x)) * 1e3 for k2, x in per.items()}
+    # per-kernel average launch duration: K back-to-back launches of one kernel
+    # between two HIP events on the launch stream (an event between every
+    # launch would add its own overhead to each)
+    us = {}
+    for name, fn in (("fwd", fwd), ("bwd_dq", bwd_dq), ("bwd_dkdv", bwd_dkdv)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us[name] = e0.elapsed_time(e1) * 1e3 / args.steps
 
     # every forward mode, for comparison (plain, online shift, exact final shift)
     fwd_modes_us = {}
@@ -240,9 +235,10 @@ def main():
 
 
 def time_path(t, w, nss, stream, mode, reps, sets=None):
-    """Mean HIP-event microseconds of attn_fwd, attn_bwd_dq and attn_bwd_dkdv
-    over `reps` steps, rotating over the input sets given (default: one)."""
-    import numpy as np
+    """Mean microseconds per step (attn_fwd, attn_bwd_dq, attn_bwd_dkdv; two HIP
+    events around `reps` steps) and per kernel (`reps` back-to-back launches of
+    one kernel between two events), rotating over the input sets given
+    (default: one)."""
     import torch
     sets = sets or [t]
     B, H, N, D = w.B, w.H, w.N, w.D
@@ -256,36 +252,43 @@ def time_path(t, w, nss, stream, mode, reps, sets=None):
                      "delta": torch.empty((B, H, N), dtype=torch.float32, device=dev)})
     kw = dict(scale=w.scale, causal=w.causal, stream=stream)
 
-    def run(i, ev=None):
+    def fwd(i):
         x, b = sets[i % len(sets)], bufs[i % len(sets)]
-        if ev:
-            ev[0].record(stream)
         nss.attn_fwd(x["q"], x["k"], x["v"], b["o"], b["lse"], b["ties"], b["pone"], None, stabilise=mode,
                      beta=w.beta, **kw)
-        if ev:
-            ev[1].record(stream)
+
+    def bwd_dq(i):
+        x, b = sets[i % len(sets)], bufs[i % len(sets)]
         nss.attn_bwd_dq(x["q"], x["k"], x["v"], b["o"], x["dO"], b["lse"], b["dq"], b["delta"], **kw)
-        if ev:
-            ev[2].record(stream)
+
+    def bwd_dkdv(i):
+        x, b = sets[i % len(sets)], bufs[i % len(sets)]
         nss.attn_bwd_dkdv(x["q"], x["k"], x["v"], x["dO"], b["lse"], b["delta"], b["dk"], b["dv"], **kw)
-        if ev:
-            ev[3].record(stream)
+
+    def step(i):
+        fwd(i)
+        bwd_dq(i)
+        bwd_dkdv(i)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
 
     for i in range(3 * len(sets)):
-        run(i)
+        step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
-    for i in range(reps):
-        run(i, evs[i])
-    torch.cuda.synchronize()
-    us = {"fwd": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3,
-          "bwd_dq": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3,
-          "bwd_dkdv": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3}
+    step_us = timed(step)
+    us = {"fwd": timed(fwd), "bwd_dq": timed(bwd_dq), "bwd_dkdv": timed(bwd_dkdv)}
     fwd_us, bwd_us = us["fwd"], us["bwd_dq"] + us["bwd_dkdv"]
-    return {"kernels_us": us, "fwd_us": fwd_us, "bwd_us": bwd_us,
+    return {"step_us": step_us, "kernels_us": us, "fwd_us": fwd_us, "bwd_us": bwd_us,
             "fwd_tflops": w.fwd_flops() / (fwd_us * 1e-6) / 1e12,
             "bwd_tflops": w.bwd_flops() / (bwd_us * 1e-6) / 1e12,
-            "fwd_bwd_tflops": (w.fwd_flops() + w.bwd_flops()) / ((fwd_us + bwd_us) * 1e-6) / 1e12}
+            "fwd_bwd_tflops": (w.fwd_flops() + w.bwd_flops()) / (step_us * 1e-6) / 1e12}
 
 
 def cold_cache(t, w, nss, stream, args):

@@ -52,9 +52,6 @@
 #define NSS_DKDV_BQ 64
 #endif
 
-#ifndef NSS_FWD_STAGES
-#define NSS_FWD_STAGES 2
-#endif
 // LDS swizzle of the forward kernels' K/V tiles (see Tile): 0 keeps them at
 // three waves per SIMD for D = 64
 #ifndef NSS_FWD_SWZ
@@ -110,15 +107,18 @@ __device__ __forceinline__ void wait_vmem_le() {
 }
 
 // eight fp32 accumulator values -> the bf16 B operand of the next contraction.
-// k-slice m (0 or 1) takes elements 4m..4m+3 and 8+4m..8+4m+3, i.e. score
-// rows 8m + 4h + {0..3} and 16 + 8m + 4h + {0..3}: the two row quads of one
-// k-slice are 16 rows apart, so the transposed LDS reads of the other operand
-// (Tile::trans8) sit at a constant offset from each other.
+// SPLIT = 16: k-slice m (0 or 1) takes elements 4m..4m+3 and 8+4m..8+4m+3,
+// i.e. score rows 8m + 4h + {0..3} and 16 + 8m + 4h + {0..3} (two row quads 16
+// rows apart); SPLIT = 8: elements 8m..8m+7, rows 16m + 4h + {0..3} and
+// 16m + 8 + 4h + {0..3}.  The other operand's transposed LDS reads
+// (Tile::trans8) follow the same pairing.
+template <int SPLIT>
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int m) {
+  static_assert(SPLIT == 8 || SPLIT == 16, "row pairing");
   bf16x8 r;
 #pragma unroll
   for (int t = 0; t < 8; t += 2) {
-    const int e = (t < 4 ? 4 * m : 8 + 4 * m) + (t & 3);
+    const int e = SPLIT == 16 ? (t < 4 ? 4 * m : 8 + 4 * m) + (t & 3) : 8 * m + t;
     bf16x2 p = __builtin_convertvector(f32x2{s[e], s[e + 1]}, bf16x2);
     r[t] = p[0];
     r[t + 1] = p[1];
@@ -139,16 +139,17 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int m) {
 // The transposed reads (32 lanes: 4 consecutive rows x 4 chunks) are
 // conflict-free too: for D = 64 rows r and r + 2 differ in bit 2 of f, for
 // D = 128 rows r .. r + 3 differ in bits 2-3.  f depends on r mod 16 only, so
-// the rows r and r + 16 one trans8 call reads share an address pattern.
-// Because f depends on r3, the two k-slices of a 32-row block (8 rows apart)
-// need separate LDS addresses; SW = 0 selects the older f = r2 | r0 << 1 |
-// r1 << 2 (distinct banks within 8 rows only: the 16-lane row reads take two
-// passes) that keeps every trans8 read at a constant offset, for a kernel
-// that cannot spare the registers.
+// the rows r and r + 16 one trans8 call reads (pairing SPLIT = 16) share an
+// address pattern.  Because f depends on r3, the two k-slices of a 32-row block
+// (8 rows apart) need separate LDS addresses; SW = 0 selects the older
+// f = r2 | r0 << 1 | r1 << 2 (distinct banks within 8 rows only: the 16-lane
+// row reads take two passes), which depends on r mod 8 only, with the pairing
+// SPLIT = 8, for a kernel that cannot spare the registers.
 // ---------------------------------------------------------------------------
 template <int D, int SW = 1>
 struct Tile {
   static constexpr int CPR = D / 8;
+  static constexpr int SPLIT = SW == 0 ? 8 : 16;  // row pairing of pack8 / trans8
   __device__ static __forceinline__ int swz(int r) {
     const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
     if constexpr (SW == 0) return r2 | (r0 << 1) | (r1 << 2);
@@ -167,14 +168,15 @@ struct Tile {
     return __builtin_bit_cast(u32x2, v);
   }
   // A operand of X^T for k-slice m of the 32 tile rows from r0 (the pairing of
-  // pack8): for lane l, column 32*cb + l%32, tile rows r0 + 8m + 4h + {0..3}
-  // and r0 + 16 + 8m + 4h + {0..3}.
+  // pack8<SPLIT>): for lane l, column 32*cb + l%32, tile rows r0 + 8m + 4h +
+  // {0..3} and r0 + 16 + 8m + 4h + {0..3} (SPLIT = 16), or r0 + 16m + 4h +
+  // {0..3} and r0 + 16m + 8 + 4h + {0..3} (SPLIT = 8).
   __device__ static __forceinline__ bf16x8 trans8(const uint16_t* t, int r0, int m, int cb, int lane) {
     const int L = lane & 15, h = lane >> 5, G = (lane >> 4) & 1;
-    const int r = r0 + 8 * m + 4 * h + (L >> 2);
+    const int r = r0 + (SPLIT == 16 ? 8 : 16) * m + 4 * h + (L >> 2);
     const int col = 32 * cb + 16 * G + 4 * (L & 3);
     const u32x2 a = tr4(t, r, col);
-    const u32x2 b = tr4(t, r + 16, col);
+    const u32x2 b = tr4(t, r + SPLIT, col);
     return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
   }
 };
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   using F = Fwd<D, BN, CAUSAL, TIES_ONLY>;
   constexpr int BM = F::BM, NKB = F::NKB, NKK = F::NKK, NCB = F::NCB, TILE = F::TILE;
   constexpr int NT = TIES_ONLY ? 1 : 2;  // K (and V) per stage
-  constexpr int NS = NSS_FWD_STAGES;      // LDS stages: tiles in flight = NS - 1
+  constexpr int NS = 2;                   // LDS stages: tiles in flight = NS - 1
   constexpr int LOADS = NT * (TILE / 8 / 256);  // 16-byte loads per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t lds[NS * NT * TILE];
 
@@ -290,18 +292,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   int c_run = 0, ones = 0;
   const bool count_ones = FORMED != nullptr;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt % NS;
+  // one KV tile; with two LDS stages the buffer is a compile-time constant
+  // (the loop is unrolled by two), so every LDS address is a loop-invariant
+  // register plus an immediate offset
+  auto tile = [&](const int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     // tile kt has landed once only the later tiles' loads are outstanding
     if (kt + NS - 2 < nkt) wait_vmem_le<LOADS * (NS - 2)>();
     else wait_vmem();
     __syncthreads();
-    if (kt + NS - 1 < nkt) fetch(kt + NS - 1, (kt + NS - 1) % NS);
+    if (kt + NS - 1 < nkt) fetch(kt + NS - 1, buf ^ 1);
     const uint16_t* Kt = lds + buf * NT * TILE;
     const uint16_t* Vt = Kt + TILE;
     const int k0 = kt * BN;
     const bool active = qw < N && (!CAUSAL || k0 <= qw + 31);
-    if (!active) continue;
+    if (!active) return;
 
     // every LDS operand of the tile is requested up front: the K rows feed the
     // score MFMAs, the transposed V reads complete under the softmax VALU work
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 p0 = pack8(s[kb], 0), p1 = pack8(s[kb], 1);
+        const bf16x8 p0 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 0), p1 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           oacc[cb] = mfma(va[kb][0][cb], p0, oacc[cb]);
@@ -387,6 +392,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
         }
       }
     }
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    tile(kt, IntC<0>{});
+    if (kt + 1 < nkt) tile(kt + 1, IntC<1>{});
   }
 
   if (qw >= N) return;
@@ -488,8 +497,9 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
   int ones = 0;
   const bool count_ones = FORMED != nullptr;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
+  // one KV tile (LDS buffer a compile-time constant, as in fwd_kernel)
+  auto tile = [&](const int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     wait_vmem();
     __syncthreads();
     if (kt + 1 < nkt) fetch(kt + 1, buf ^ 1);
@@ -497,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
     const uint16_t* Vt = Kt + TILE;
     const int k0 = kt * BN;
     const bool active = qw < N && (!CAUSAL || k0 <= qw + 31);
-    if (!active) continue;
+    if (!active) return;
 
     bf16x8 ka[NKB][NKK];
 #pragma unroll
@@ -543,13 +553,17 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const bf16x8 p0 = pack8(s[kb], 0), p1 = pack8(s[kb], 1);
+      const bf16x8 p0 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 0), p1 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 1);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         oacc[cb] = mfma(va[kb][0][cb], p0, oacc[cb]);
         oacc[cb] = mfma(va[kb][1][cb], p1, oacc[cb]);
       }
     }
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    tile(kt, IntC<0>{});
+    if (kt + 1 < nkt) tile(kt + 1, IntC<1>{});
   }
 
   if (qw >= N) return;
@@ -680,7 +694,7 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
         const float p = exp2f_fast(__builtin_fmaf(s[r], t, -lse2));
         s[r] = p * dp[r];
       }
-      const bf16x8 d0 = pack8(s, 0), d1 = pack8(s, 1);
+      const bf16x8 d0 = pack8<Tile<D>::SPLIT>(s, 0), d1 = pack8<Tile<D>::SPLIT>(s, 1);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         dqa[cb] = mfma(Tile<D>::trans8(Kt, 32 * kb, 0, cb, lane), d0, dqa[cb]);
@@ -814,8 +828,8 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_ke
             dp[r] = p * dp[r];
           }
         }
-        const bf16x8 p0 = pack8(s, 0), p1 = pack8(s, 1);
-        const bf16x8 d0 = pack8(dp, 0), d1 = pack8(dp, 1);
+        const bf16x8 p0 = pack8<Tile<D>::SPLIT>(s, 0), p1 = pack8<Tile<D>::SPLIT>(s, 1);
+        const bf16x8 d0 = pack8<Tile<D>::SPLIT>(dp, 0), d1 = pack8<Tile<D>::SPLIT>(dp, 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           dva[cb] = mfma(Tile<D>::trans8(Gt, 32 * qb, 0, cb, lane), p0, dva[cb]);
