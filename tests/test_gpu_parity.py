@@ -31,6 +31,9 @@ SMALL = [
     (1, 1, 1, 64, True, 17, 0),
     (1, 1, 1, 128, False, 18, 0),
     (1, 1, 64, 128, True, 19, 4),
+    # B*H a multiple of 8: the XCD-grouped workgroup order, with ragged tails
+    (1, 8, 1000, 64, True, 22, 10),
+    (2, 4, 777, 128, False, 23, 0),
 ]
 
 
