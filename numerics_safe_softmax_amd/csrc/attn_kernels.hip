@@ -52,8 +52,12 @@
 #define NSS_DKDV_BQ 64
 #endif
 
-// LDS swizzle of the forward kernels' K/V tiles (see Tile): 0 keeps them at
-// three waves per SIMD for D = 64
+// workgroups per CU the D = 64 forward is compiled for (4: 128 VGPRs)
+#ifndef NSS_FWD_WGS
+#define NSS_FWD_WGS 4
+#endif
+// LDS swizzle of the forward kernels' K/V tiles (see Tile): 0 keeps their
+// register count down for D = 64
 #ifndef NSS_FWD_SWZ
 #define NSS_FWD_SWZ 0
 #endif
@@ -247,7 +251,7 @@ struct Fwd {
 };
 
 template <int D, int BN, bool CAUSAL, bool TIES_ONLY>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(
+__global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ O32, float* __restrict__ LSE, int32_t* __restrict__ TIES,
     int32_t* __restrict__ PONE, int32_t* __restrict__ FORMED, float* __restrict__ ROWMAX,
@@ -308,29 +312,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     const bool active = qw < N && (!CAUSAL || k0 <= qw + 31);
     if (!active) return;
 
-    // every LDS operand of the tile is requested up front: the K rows feed the
-    // score MFMAs, the transposed V reads complete under the softmax VALU work
-    bf16x8 ka[NKB][NKK];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = Tile<D, kFwdSW>::row8(Kt, 32 * kb + li, 2 * kk + h);
+    // LDS operands are read where they are used (no up-front copy of the
+    // tile's K and V operands): 128 VGPRs, 4 waves per SIMD at d = 64
     f32x16 s[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma(ka[kb][kk], qf[kk], s[kb]);
-    bf16x8 va[TIES_ONLY ? 1 : NKB][2][NCB];
-    if constexpr (!TIES_ONLY) {
-#pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) va[kb][m][cb] = Tile<D, kFwdSW>::trans8(Vt, 32 * kb, m, cb, lane);
-    }
+        s[kb] = mfma(Tile<D, kFwdSW>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
     if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -387,8 +378,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
         const bf16x8 p0 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 0), p1 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          oacc[cb] = mfma(va[kb][0][cb], p0, oacc[cb]);
-          oacc[cb] = mfma(va[kb][1][cb], p1, oacc[cb]);
+          oacc[cb] = mfma(Tile<D, kFwdSW>::trans8(Vt, 32 * kb, 0, cb, lane), p0, oacc[cb]);
+          oacc[cb] = mfma(Tile<D, kFwdSW>::trans8(Vt, 32 * kb, 1, cb, lane), p1, oacc[cb]);
         }
       }
     }
@@ -456,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 // natural-log log-sum-exp.
 // ---------------------------------------------------------------------------
 template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
+__global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ O32, float* __restrict__ LSE, int32_t* __restrict__ FORMED, int BH,
     int N, float scale,
@@ -509,25 +500,14 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
     const bool active = qw < N && (!CAUSAL || k0 <= qw + 31);
     if (!active) return;
 
-    bf16x8 ka[NKB][NKK];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) ka[kb][kk] = Tile<D, kFwdSW>::row8(Kt, 32 * kb + li, 2 * kk + h);
     f32x16 s[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma(ka[kb][kk], qf[kk], s[kb]);
-    bf16x8 va[NKB][2][NCB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) va[kb][m][cb] = Tile<D, kFwdSW>::trans8(Vt, 32 * kb, m, cb, lane);
+      for (int kb = 0; kb < NKB; ++kb)
+        s[kb] = mfma(Tile<D, kFwdSW>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
     if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -556,8 +536,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fixed_kernel(
       const bf16x8 p0 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 0), p1 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 1);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        oacc[cb] = mfma(va[kb][0][cb], p0, oacc[cb]);
-        oacc[cb] = mfma(va[kb][1][cb], p1, oacc[cb]);
+        oacc[cb] = mfma(Tile<D, kFwdSW>::trans8(Vt, 32 * kb, 0, cb, lane), p0, oacc[cb]);
+        oacc[cb] = mfma(Tile<D, kFwdSW>::trans8(Vt, 32 * kb, 1, cb, lane), p1, oacc[cb]);
       }
     }
   };
