@@ -703,13 +703,18 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
 // dP = dO V^T, dS = P (dP - delta), dV^T += dO^T P, dK^T += Q^T dS.
 // ---------------------------------------------------------------------------
 template <int D, int BQ, bool CAUSAL>
-__global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, NSS_DKDV_WAVES) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale, int nkt) {
   constexpr int BK = 128, NQB = BQ / 32, NKK = D / 16, NCB = D / 32, TILE = BQ * D;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];
   __shared__ __attribute__((aligned(16))) float rowv[2][2][BQ];  // [buf][lse2, delta][row]
+  // d = 128: the workgroup's V rows sit in LDS (32 KB) and are read as the dP
+  // products' B operand where used, instead of 32 VGPRs per lane: the kernel
+  // then fits 2 waves per SIMD (long_context dK/dV 709 -> 522 us)
+  constexpr bool VL = (D == 128);
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[VL ? BK * D : 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -742,15 +747,16 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_ke
       rowv[buf][1][tid] = -rd;  // -delta: the initial value of the dP accumulator
     }
   };
+  if constexpr (VL) tile_to_lds<BK, D>(V + head, k0, N, vtile, wu, lane);  // rows past N: row N-1, unused
   fetch(qstart, 0);
 
-  bf16x8 kf[NKK], vf[NKK];
+  bf16x8 kf[NKK], vf[VL ? 1 : NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     const size_t off = head + (size_t)kj * D + 16 * kk + 8 * h;
     const u32x4 z{0, 0, 0, 0};
     kf[kk] = as_bf16x8(kj < N ? ld16(K + off) : z);
-    vf[kk] = as_bf16x8(kj < N ? ld16(V + off) : z);
+    if constexpr (!VL) vf[kk] = as_bf16x8(kj < N ? ld16(V + off) : z);
   }
   f32x16 dka[NCB], dva[NCB];
 #pragma unroll
@@ -788,7 +794,11 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_DKDV_WAVES : 1) void bwd_dkdv_ke
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
           s = mfma(Tile<D>::row8(Qt, 32 * qb + li, 2 * kk + h), kf[kk], s);
-          dp = mfma(Tile<D>::row8(Gt, 32 * qb + li, 2 * kk + h), vf[kk], dp);
+          if constexpr (VL)
+            dp = mfma(Tile<D>::row8(Gt, 32 * qb + li, 2 * kk + h), Tile<D>::row8(vtile, 32 * wu + li, 2 * kk + h),
+                      dp);
+          else
+            dp = mfma(Tile<D>::row8(Gt, 32 * qb + li, 2 * kk + h), vf[kk], dp);
         }
         if ((CAUSAL && r0 + 32 * qb < kw + 31) || r0 + 32 * qb + 32 > N) {
 #pragma unroll
