@@ -51,6 +51,9 @@
 #ifndef NSS_DKDV_BQ
 #define NSS_DKDV_BQ 64
 #endif
+#ifndef NSS_DKDV_PF
+#define NSS_DKDV_PF 1
+#endif
 
 // workgroups per CU the D = 64 forward is compiled for (4: 128 VGPRs)
 #ifndef NSS_FWD_WGS
@@ -708,13 +711,22 @@ __global__ __launch_bounds__(256, NSS_DKDV_WAVES) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale, int nkt) {
   constexpr int BK = 128, NQB = BQ / 32, NKK = D / 16, NCB = D / 32, TILE = BQ * D;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];
-  __shared__ __attribute__((aligned(16))) float rowv[2][2][BQ];  // [buf][lse2, delta][row]
   // d = 128: the workgroup's V rows sit in LDS (32 KB) and are read as the dP
   // products' B operand where used, instead of 32 VGPRs per lane: the kernel
   // then fits 2 waves per SIMD (long_context dK/dV 709 -> 522 us)
   constexpr bool VL = (D == 128);
   __shared__ __attribute__((aligned(16))) uint16_t vtile[VL ? BK * D : 8];
+  // d = 64: each block's LDS operands are read ahead of their use, and each
+  // LDS stage is a variable of its own: reading one stage then cannot alias
+  // the global->LDS loads into the other, so the compiler does not wait for
+  // the prefetch of the next tile before the first LDS reads of this one
+  // (at d = 128 the single buffer measured faster)
+  constexpr bool PF = !VL && NSS_DKDV_PF;
+  __shared__ __attribute__((aligned(16))) uint16_t ldsA[PF ? 2 * TILE : 4 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t ldsB[PF ? 2 * TILE : 8];
+  uint16_t* const lds0 = ldsA;
+  uint16_t* const lds1 = PF ? ldsB : ldsA + 2 * TILE;
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][BQ];  // [buf][lse2, delta][row]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -730,25 +742,24 @@ __global__ __launch_bounds__(256, NSS_DKDV_WAVES) void bwd_dkdv_kernel(
   const int qstart = CAUSAL ? (k0 / BQ) : 0;
   const int nqt = (N + BQ - 1) / BQ;
   float rl = 0.f, rd = 0.f;
-  auto fetch = [&](int qt, int buf) {
-    uint16_t* base = lds + buf * 2 * TILE;
+  auto fetch = [&](int qt, uint16_t* base) {
     tile_to_lds<BQ, D>(Q + head, qt * BQ, N, base, wu, lane);
     tile_to_lds<BQ, D>(dO + head, qt * BQ, N, base + TILE, wu, lane);
     if (tid < BQ) {
       int r = qt * BQ + tid;
       r = r < N ? r : N - 1;
-      rl = LSE[hrow + r] * kLog2e;
+      rl = LSE[hrow + r];
       rd = DELTA[hrow + r];
     }
   };
   auto commit_rows = [&](int buf) {
     if (tid < BQ) {
-      rowv[buf][0][tid] = rl;
+      rowv[buf][0][tid] = rl * kLog2e;
       rowv[buf][1][tid] = -rd;  // -delta: the initial value of the dP accumulator
     }
   };
   if constexpr (VL) tile_to_lds<BK, D>(V + head, k0, N, vtile, wu, lane);  // rows past N: row N-1, unused
-  fetch(qstart, 0);
+  fetch(qstart, lds0);
 
   bf16x8 kf[NKK], vf[VL ? 1 : NKK];
 #pragma unroll
@@ -773,8 +784,8 @@ __global__ __launch_bounds__(256, NSS_DKDV_WAVES) void bwd_dkdv_kernel(
     constexpr int buf = decltype(bufc)::value;
     wait_vmem();
     __syncthreads();
-    if (qt + 1 < nqt) fetch(qt + 1, buf ^ 1);
-    const uint16_t* Qt = lds + buf * 2 * TILE;
+    if (qt + 1 < nqt) fetch(qt + 1, buf ? lds0 : lds1);
+    const uint16_t* Qt = buf ? lds1 : lds0;
     const uint16_t* Gt = Qt + TILE;
     const int r0 = qt * BQ;
     const bool active = kw < N && (!CAUSAL || r0 + BQ - 1 >= kw);
@@ -783,6 +794,72 @@ __global__ __launch_bounds__(256, NSS_DKDV_WAVES) void bwd_dkdv_kernel(
       // the live score registers)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
+        if constexpr (PF) {
+          // every LDS operand of the block is read ahead of its use: the S
+          // and dP operands before their products, and the dV / dK operands
+          // right behind those products, so that their latency hides behind
+          // the products and the vector work instead of stalling each
+          // product pair
+          f32x4 d4[4], l4[4];
+          bf16x8 qa[NKK], ga[NKK];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            d4[g] = *reinterpret_cast<const f32x4*>(&rowv[buf][1][32 * qb + 8 * g + 4 * h]);
+            l4[g] = *reinterpret_cast<const f32x4*>(&rowv[buf][0][32 * qb + 8 * g + 4 * h]);
+          }
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            qa[kk] = Tile<D>::row8(Qt, 32 * qb + li, 2 * kk + h);
+            ga[kk] = Tile<D>::row8(Gt, 32 * qb + li, 2 * kk + h);
+          }
+          // dP accumulates onto -delta, so dP - delta comes out of the products
+          f32x16 s = f32x16{}, dp;
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) dp[4 * g + jj] = d4[g][jj];
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            s = mfma(qa[kk], kf[kk], s);
+            dp = mfma(ga[kk], vf[kk], dp);
+          }
+          bf16x8 tg[NCB][2], tq[NCB][2];
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              tg[cb][m] = Tile<D>::trans8(Gt, 32 * qb, m, cb, lane);
+              tq[cb][m] = Tile<D>::trans8(Qt, 32 * qb, m, cb, lane);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+          if ((CAUSAL && r0 + 32 * qb < kw + 31) || r0 + 32 * qb + 32 > N) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int qrow = r0 + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
+              if ((CAUSAL && qrow < kj) || qrow >= N) s[r] = -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int r = 4 * g + jj;
+              const float p = exp2f_fast(__builtin_fmaf(s[r], t, -l4[g][jj]));
+              s[r] = p;
+              dp[r] = p * dp[r];
+            }
+          const bf16x8 p0 = pack8<Tile<D>::SPLIT>(s, 0), p1 = pack8<Tile<D>::SPLIT>(s, 1);
+          const bf16x8 d0 = pack8<Tile<D>::SPLIT>(dp, 0), d1 = pack8<Tile<D>::SPLIT>(dp, 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            dva[cb] = mfma(tg[cb][0], p0, dva[cb]);
+            dva[cb] = mfma(tg[cb][1], p1, dva[cb]);
+            dka[cb] = mfma(tq[cb][0], d0, dka[cb]);
+            dka[cb] = mfma(tq[cb][1], d1, dka[cb]);
+          }
+          continue;
+        }
         // dP accumulates onto -delta, so dP - delta comes out of the products
         f32x16 s = f32x16{}, dp;
 #pragma unroll
