@@ -282,6 +282,18 @@ def time_path(t, w, nss, stream, mode, reps, sets=None):
     for i in range(3 * len(sets)):
         step(i)
     torch.cuda.synchronize()
+    # an idle GPU needs tens of milliseconds of load to reach its working
+    # clock: warm up for about 50 ms, and time at least about 25 ms per figure
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < 0.05:
+        step(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    per_step = (time.perf_counter() - t0) / i
+    reps = max(reps, int(0.025 / per_step) + 1)
     step_us = timed(step)
     us = {"fwd": timed(fwd), "bwd_dq": timed(bwd_dq), "bwd_dkdv": timed(bwd_dkdv)}
     fwd_us, bwd_us = us["fwd"], us["bwd_dq"] + us["bwd_dkdv"]
