@@ -197,6 +197,16 @@ def main():
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "algorithmic_bytes": bytes_dom, "avg_launch_us": us[dom]}
 
+    # every kernel against both ceilings: its algorithmic flops against the
+    # bf16 MFMA peak and its compulsory bytes against the 8 TB/s HBM peak
+    per_kernel = {}
+    for name, (fl, by) in kinfo.items():
+        t_s = us[name] * 1e-6
+        per_kernel[name] = {"avg_launch_us": us[name], "tflops": fl / t_s / 1e12,
+                            "frac_mfma": fl / t_s / 1e12 / PEAK_BF16_TFLOPS,
+                            "algorithmic_GBps": by / t_s / 1e9, "frac_hbm": by / t_s / 1e9 / PEAK_HBM_GBS,
+                            "traffic": measured_traffic(name)}
+
     out = {
         "metric": METRIC,
         "value": tflops,
@@ -223,6 +233,7 @@ def main():
         "bwd_tflops": bwd_flops / ((us["bwd_dq"] + us["bwd_dkdv"]) * 1e-6) / 1e12,
         "fwd_modes_us": fwd_modes_us,
         "roofline": roofline,
+        "kernels_roofline": per_kernel,
         "cpu_baseline": None,
     }
 
