@@ -2,10 +2,20 @@
 and compare it element by element with the FP64 oracle."""
 from __future__ import annotations
 
+import contextlib
+import dataclasses
+import json
+import os
+import re
+
 import numpy as np
 
 import oracle
 from numerics_safe_softmax_amd import inputs
+
+# where a failing case's inputs are recorded (gpurun_out/ comes back from a GPU run)
+FAIL_DIR = os.environ.get("NSS_FAIL_DIR", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                                       "gpurun_out", "failures"))
 
 FWD_WANT = ["O", "tol_O", "lse", "tol_lse", "ties", "pbar_one", "amb_tie", "amb_pbar", "amb_near",
             "near_ones", "rowmax", "flags"]
@@ -80,3 +90,42 @@ def check_backward(b, rb, heads=None, label=""):
     assert r <= 1.0, "%s delta max err/tol %.3f" % (label, r)
     out["delta"] = r
     return out
+
+
+def dump_case(path, d, w, mode, note=""):
+    """Record one case: the bf16 bit patterns of every input (uint16 .npy), the
+    workload that generated them and the mode, so that it can be replayed
+    without regenerating (tests/replay.py)."""
+    os.makedirs(path, exist_ok=True)
+    for name, bits in d.items():
+        np.save(os.path.join(path, name + ".npy"), np.ascontiguousarray(bits, dtype=np.uint16))
+    meta = {"workload": dataclasses.asdict(w), "mode": int(mode), "note": note}
+    with open(os.path.join(path, "case.json"), "w") as fh:
+        json.dump(meta, fh, indent=1)
+    return path
+
+
+def load_case(path):
+    """The inputs, workload and mode recorded by dump_case."""
+    with open(os.path.join(path, "case.json")) as fh:
+        meta = json.load(fh)
+    w = inputs.Workload(**meta["workload"])
+    d = {}
+    for fn in sorted(os.listdir(path)):
+        if fn.endswith(".npy"):
+            d[fn[:-4]] = np.load(os.path.join(path, fn))
+    return d, w, meta["mode"]
+
+
+@contextlib.contextmanager
+def record_on_failure(label, d, w, mode):
+    """Run the checks in the block; if one fails, record the case's inputs under
+    FAIL_DIR before the failure propagates."""
+    try:
+        yield
+    except AssertionError as e:
+        where = dump_case(os.path.join(FAIL_DIR, re.sub(r"[^A-Za-z0-9_.-]+", "_", label).strip("_")), d, w, mode,
+                          note=str(e))
+        print("recorded failing case in %s" % where, flush=True)
+        raise
+

@@ -63,19 +63,20 @@ def test_small_fwd_bwd_parity(case, mode):
     ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=mode != 0,
                          beta=w.beta)
     rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=w.causal)
-    fr = parity.check_forward(f, ref, label=str(case))
-    br = parity.check_backward(b, rb, label=str(case))
-    _say("  fwd %s bwd %s" % (fr, br))
-    formed = f["formed_ones"].cpu().numpy()
-    ok = ref["amb_tie"] == 0
-    if mode == 0:
-        # plain rows: each tied maximum is fed to P_bar V as an exact bf16 1.0
-        assert np.all(formed[ok] >= ref["ties"][ok])
-        assert np.all(f["pbar_one"].cpu().numpy() == 1)
-    if mode == 2:
-        # the exact-final-shift kernel forms exactly the bf16 ones the final shift predicts
-        okn = ok & (ref["amb_near"] == 0)
-        assert np.array_equal(formed[okn], ref["near_ones"][okn])
+    with parity.record_on_failure("parity_%s_m%d" % (case, mode), d, w, mode):
+        fr = parity.check_forward(f, ref, label=str(case))
+        br = parity.check_backward(b, rb, label=str(case))
+        _say("  fwd %s bwd %s" % (fr, br))
+        formed = f["formed_ones"].cpu().numpy()
+        ok = ref["amb_tie"] == 0
+        if mode == 0:
+            # plain rows: each tied maximum is fed to P_bar V as an exact bf16 1.0
+            assert np.all(formed[ok] >= ref["ties"][ok])
+            assert np.all(f["pbar_one"].cpu().numpy() == 1)
+        if mode == 2:
+            # the exact-final-shift kernel forms exactly the bf16 ones the final shift predicts
+            okn = ok & (ref["amb_near"] == 0)
+            assert np.array_equal(formed[okn], ref["near_ones"][okn])
 
 
 @pytest.mark.parametrize("case", SMALL[:5], ids=lambda c: "B%dH%dN%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n"))

@@ -60,5 +60,6 @@ def test_sweep_parity(case):
     torch.cuda.synchronize()
     ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=mode != 0, beta=w.beta)
     rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=w.causal)
-    parity.check_forward(f, ref, label=str(case))
-    parity.check_backward(b, rb, label=str(case))
+    with parity.record_on_failure("sweep_%s" % (case,), d, w, mode):
+        parity.check_forward(f, ref, label=str(case))
+        parity.check_backward(b, rb, label=str(case))
