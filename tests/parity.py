@@ -13,9 +13,11 @@ import numpy as np
 import oracle
 from numerics_safe_softmax_amd import inputs
 
-# where a failing case's inputs are recorded (gpurun_out/ comes back from a GPU run)
-FAIL_DIR = os.environ.get("NSS_FAIL_DIR", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                                                       "gpurun_out", "failures"))
+# where the GPU tests write their reports and record failing cases
+# (NSS_REPORT_DIR, default test_reports/ at the repository root)
+REPORT_DIR = os.environ.get("NSS_REPORT_DIR",
+                            os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "test_reports"))
+FAIL_DIR = os.path.join(REPORT_DIR, "failures")
 
 FWD_WANT = ["O", "tol_O", "lse", "tol_lse", "ties", "pbar_one", "amb_tie", "amb_pbar", "amb_near",
             "near_ones", "rowmax", "flags"]

@@ -1,6 +1,6 @@
 """Replay a recorded parity case on the GPU against the oracle.
 
-    python -m tests.replay gpurun_out/failures/<case>
+    python -m tests.replay test_reports/failures/<case>
 
 Loads the bf16 inputs, workload and mode that tests/parity.py recorded when a
 check failed, runs the C-ABI forward and backward on cuda:0 and the FP64

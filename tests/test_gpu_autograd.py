@@ -5,7 +5,7 @@ oracle within tolerance; the layer is trained for a few SGD steps on
 synthetic repeated-token inputs (identical keys, hence repeated row maxima)
 in each mode, and at every step the attention inside it is checked against
 the oracle and the signed bias of O and delta on tie rows is recorded
-(gpurun_out/layer_bias.json).
+(layer_bias.json in the report directory, tests/parity.py).
 """
 import json
 import os
@@ -106,8 +106,7 @@ def test_gpt2_layer_bias_over_steps():
         report[{0: "plain", 1: "online_shift", 2: "exact_shift"}[mode]] = steps
         assert steps[-1]["loss"] < steps[0]["loss"]
         assert steps[0]["tie_rows"] > 0
-    out = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
-    if os.path.isdir(out):
-        with open(os.path.join(out, "layer_bias.json"), "w") as fh:
-            json.dump(report, fh, indent=1)
+    os.makedirs(parity.REPORT_DIR, exist_ok=True)
+    with open(os.path.join(parity.REPORT_DIR, "layer_bias.json"), "w") as fh:
+        json.dump(report, fh, indent=1)
     print(json.dumps(report), flush=True)

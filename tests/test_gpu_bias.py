@@ -6,7 +6,7 @@ accumulation of P_bar V drifts O negative; section "极简修复方案": the shi
 keeps max(P_bar) below 1 on those rows.  Here: the event counts are checked
 exactly against the oracle's prediction; the signed error of O and delta on
 tie rows x negatively skewed V dimensions is measured against the FP64 oracle
-and written to gpurun_out/bias_report.json.
+and written to bias_report.json in the report directory (tests/parity.py).
 """
 import json
 import os
@@ -105,10 +105,9 @@ def test_events_and_bias(wname, heads):
         res["stabilised"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"],
         res["unstabilised"]["vs_rounded_reference"]["O_tie_rows_skewed_dims"])
     REPORT[wname] = res
-    out = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
-    if os.path.isdir(out):
-        with open(os.path.join(out, "bias_report.json"), "w") as fh:
-            json.dump(REPORT, fh, indent=1)
+    os.makedirs(parity.REPORT_DIR, exist_ok=True)
+    with open(os.path.join(parity.REPORT_DIR, "bias_report.json"), "w") as fh:
+        json.dump(REPORT, fh, indent=1)
     zs = {m: res[m]["vs_rounded_reference"]["O_tie_rows_skewed_dims"]["z"]
           for m in ("unstabilised", "stabilised", "stabilised_exact")}
     print("  O bias z on tie rows (vs rounded FP64): plain %.2f, online shift %.2f, exact shift %.2f" % (
