@@ -91,9 +91,9 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(attention heads shard across GPUs with no exchange; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (attention heads "
+              "would shard across GPUs with no exchange, each GPU running these kernels on its "
+              "share). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
