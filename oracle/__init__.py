@@ -95,6 +95,8 @@ def lib():
                                    ctypes.POINTER(_BwdOut)]
         L.orc_emulate_pv.restype = ctypes.c_int
         L.orc_emulate_pv.argtypes = [ctypes.POINTER(_Problem), _P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P, _P]
+        L.orc_online_ones.restype = ctypes.c_int
+        L.orc_online_ones.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int, _P, ctypes.c_int64, _P, _P]
         L.orc_threads.restype = ctypes.c_int
         L.orc_threads.argtypes = []
         _lib = L
@@ -247,6 +249,27 @@ def emulate_bf16_pv(q, k, v, *, scale: float, causal: bool, stabilise: bool = Fa
     if rc != 0:
         raise ValueError("oracle emulation rejected the inputs")
     return {"O": O, "events": ev}
+
+
+def online_ones(q, k, *, scale: float, causal: bool, stabilise: bool, beta: float = 2.0, tile: int = 64,
+                rows: Optional[Sequence[int]] = None) -> dict:
+    """Keys per row whose P_bar rounds to a bf16 1.0 when the duplicate-max rule
+    is applied online: the running (max, count) merged tile by tile in key
+    order (tiles of ``tile`` keys from key 0) and each tile's P_bar formed
+    with the shift of the pair after that tile (``online_row`` in oracle.c).
+
+    Returns {"ones": [B, H, N] int32, "amb": [B, H, N] int32}; rows not
+    computed are -1.
+    """
+    p, keep, (B, H, N, D) = _problem(q, k, None, None, scale, causal, stabilise, beta)
+    ones = np.full((B, H, N), -1, dtype=np.int32)
+    amb = np.full((B, H, N), -1, dtype=np.int32)
+    rr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    rc = lib().orc_online_ones(ctypes.byref(p), int(tile), _ptr(rr), 0 if rr is None else rr.size, _ptr(ones),
+                               _ptr(amb))
+    if rc != 0:
+        raise ValueError("oracle online count rejected the inputs")
+    return {"ones": ones, "amb": amb}
 
 
 def head_rows(heads: Sequence[int], N: int) -> np.ndarray:

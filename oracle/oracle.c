@@ -558,6 +558,96 @@ int orc_forward(const orc_problem* p, const int64_t* rows, int64_t nrows, const 
 }
 
 /* ------------------------------------------------------------------ */
+/* the online rule, tile by tile                                       */
+/* ------------------------------------------------------------------ */
+
+/*
+ * [ITS] section "极简修复方案" states the rule on a whole row; a tiled kernel
+ * applies it to the running (max, count) pair, merged tile by tile in key
+ * order (larger max keeps its count, equal maxima add counts), and forms
+ * P_bar_j = exp(S_j - m*) for the keys of each tile with the shift m* of
+ * the pair as it stands after that tile.  This counts, for one row, the keys
+ * whose P_bar so formed rounds (bf16 nearest-even) to exactly 1, tiles of
+ * `tile` keys starting at key 0.  *amb is set when a running maximum could be
+ * counted differently from fp32 dot products (another key within their
+ * error of it, or tied keys that are different vectors with inexact sums),
+ * when some P_bar lies within 2^-14 of the bf16 1.0 boundary, or when the
+ * exact scores needed the slow path.
+ */
+static void online_row(const orc_problem* p, const decoded* dc, int64_t row, row_scratch* s, int tile,
+                       int32_t* ones, int32_t* amb) {
+  const int N = p->N, D = p->D;
+  const int64_t bh = row / N;
+  const int i = (int)(row % N);
+  const int jl = last_key(p, i);
+  double rm_raw;
+  int rs;
+  int ambig = row_scores(p, dc, bh, i, jl, s, &rm_raw, &rs);
+  const double gamma = 2.0 * D * U_F32;
+  double m = -INFINITY;
+  int c = 0, count = 0;
+  for (int t0 = 0; t0 <= jl; t0 += tile) {
+    const int t1 = t0 + tile - 1 < jl ? t0 + tile - 1 : jl;
+    double tm = -INFINITY;
+    int tc = 0;
+    for (int j = t0; j <= t1; ++j) {
+      if (s->raw[j] > tm) { tm = s->raw[j]; tc = 1; }
+      else if (s->raw[j] == tm) ++tc;
+    }
+    if (tm > m) { m = tm; c = tc; }
+    else if (tm == m) c += tc;
+    /* could fp32 sums decide this running pair differently? */
+    double E = 0.0;
+    int first = -1;
+    for (int j = 0; j <= t1; ++j) {
+      if (s->raw[j] != m) continue;
+      if (first < 0) first = j;
+      double e = s->f32exact[j] ? 0.0 : gamma * s->sabs[j];
+      if (e > E) E = e;
+    }
+    int nnear = 0;
+    for (int j = 0; j <= t1; ++j) {
+      double e = s->f32exact[j] ? 0.0 : gamma * s->sabs[j];
+      if (m - s->raw[j] <= e + E) ++nnear;
+    }
+    if (nnear > c) ambig = 1;
+    if (c > 1 && E > 0.0) {
+      const uint16_t* kf = p->k + (bh * N + first) * D;
+      for (int j = first + 1; j <= t1; ++j)
+        if (s->raw[j] == m && memcmp(kf, p->k + (bh * N + j) * D, sizeof(uint16_t) * (size_t)D) != 0) ambig = 1;
+    }
+    const double mstar = orc_shift_rule(p->scale * m, c, p->stabilise, p->beta);
+    for (int j = t0; j <= t1; ++j) {
+      const double pb = exp(p->scale * s->raw[j] - mstar);
+      if (orc_bf16_from_double(pb, ORC_RNE) == BF16_ONE) ++count;
+      if (fabs(pb - (1.0 - 0x1p-9)) <= 0x1p-14) ambig = 1;
+    }
+  }
+  ones[row] = count;
+  if (amb) amb[row] = ambig;
+}
+
+/* rows: flattened rows or NULL for all; ones / amb: [B][H][N]. Returns 0, or -1. */
+int orc_online_ones(const orc_problem* p, int tile, const int64_t* rows, int64_t nrows, int32_t* ones,
+                    int32_t* amb) {
+  if (p->N <= 0 || p->B <= 0 || p->H <= 0) return 0;
+  if (tile < 1 || !ones) return -1;
+  decoded dc;
+  if (decode_problem(p, &dc) != 0) { free_decoded(&dc); return -1; }
+  const int64_t total = rows ? nrows : (int64_t)p->B * p->H * p->N;
+#pragma omp parallel
+  {
+    row_scratch s;
+    scratch_init(&s, p->N);
+#pragma omp for schedule(dynamic, 8)
+    for (int64_t t = 0; t < total; ++t) online_row(p, &dc, rows ? rows[t] : t, &s, tile, ones, amb);
+    scratch_free(&s);
+  }
+  free_decoded(&dc);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* emulation of a bf16-accumulated P_bar V                             */
 /* ------------------------------------------------------------------ */
 
