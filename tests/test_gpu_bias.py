@@ -76,6 +76,22 @@ def test_events_and_bias(wname, heads):
         rep["tie_rows"] = int(tie.sum())
         rep["pbar_one_events_on_tie_rows"] = int(pone[tie].sum())
         rep["formed_ones_on_tie_rows"] = int(formed[stabilise][tie].sum())
+        # rows by the number of bf16 ones the kernel formed (tie rows / every row)
+        for name, sel in (("tie_rows", tie), ("all_rows", rmask)):
+            v = formed[stabilise][sel]
+            rep["formed_ones_histogram_" + name] = {"0": int((v == 0).sum()), "1": int((v == 1).sum()),
+                                                    "2": int((v == 2).sum()), "3": int((v == 3).sum()),
+                                                    ">=4": int((v >= 4).sum())}
+        if stabilise == 0:
+            # near ties: one maximum, but a second score close enough to round to a bf16 1 too
+            rep["near_tie_rows"] = int((rmask & (ref["ties"] == 1) & (ref["near_ones"] >= 2)).sum())
+        if stabilise in (0, 1):
+            # the formed ones, row by row, against the rule applied tile by tile
+            on = oracle.online_ones(d["q"], d["k"], scale=w.scale, causal=w.causal, stabilise=stabilise != 0,
+                                    beta=w.beta, tile=64, rows=rows)
+            dec = rmask & (on["amb"] == 0)
+            assert np.array_equal(formed[stabilise][dec], on["ones"][dec])
+            rep["online_count_rows_checked"] = int(dec.sum())
         if stabilise == 2:
             # no exact 1 is ever formed on a repeated-max row
             exn = exact & (ref["amb_near"] == 0)
