@@ -242,6 +242,7 @@ def main():
         out["other_workloads"] = other_workloads(w.name, nss, stream, args.mode)
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["bias"] = cpu_leg(w, d, nss, t, stream)
+        out["cpu_baseline"]["gpu_over_cpu"] = tflops / out["cpu_baseline"]["value"]
     print(json.dumps(out), flush=True)
 
 
@@ -344,6 +345,18 @@ def other_workloads(skip, nss, stream, mode):
     return res
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_leg(w, d, nss, t, stream):
     """The FP64 oracle on the host, on the whole workload (fwd + bwd), timed;
     its result also gives the signed-bias diagnostic of both GPU modes."""
@@ -364,7 +377,8 @@ def cpu_leg(w, d, nss, t, stream):
     cpu = {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
            "sample": "the whole %s workload (B=%d H=%d N=%d D=%d), FP64 forward + backward, "
                      "%.2f s + %.2f s" % (w.name, w.B, w.H, w.N, w.D, t1 - t0, t2 - t1),
-           "seconds": t2 - t0}
+           "seconds": t2 - t0, "fwd_seconds": t1 - t0, "bwd_seconds": t2 - t1,
+           "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
     gO = inputs_f64(d["dO"])
     res = {}
