@@ -101,9 +101,20 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_c
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Combine the two 32-lane halves (lane l and lane l ^ 32 hold the same row).
-__device__ __forceinline__ float max32(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
 __device__ __forceinline__ float sum32(float v) { return v + __shfl_xor(v, 32); }
 __device__ __forceinline__ int sum32i(int v) { return v + __shfl_xor(v, 32); }
+
+// The same exchange through the VALU (gfx950's v_permlane32_swap: the upper
+// half of one register trades places with the lower half of another) instead
+// of an LDS-crossbar round trip: with a = b = v on entry, every lane ends up
+// holding {v(l), v(l ^ 32)} in (a, b), in the same order for every call.
+// Written out because this compiler folds the builtin's second result into its
+// first; the nops cover the VALU-write -> permlane-read hazard on both sides.
+__device__ __forceinline__ void swap_halves(uint32_t v, uint32_t& a, uint32_t& b) {
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // wait until at most N vector-memory operations of this wave are outstanding
@@ -337,19 +348,28 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
           if ((CAUSAL && key > qi) || key >= N) s[kb][r] = -INFINITY;
         }
     }
-    // tile (max, count) on the raw fp32 dot products, then the running merge
+    // tile (max, count) on the raw fp32 dot products, then the running merge.
+    // Each half-row first takes its own (max, count); one exchange then merges
+    // the two halves (a half whose max is below the row's adds nothing), so the
+    // row count is exactly the number of entries equal to the row max.
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max32(mx);
     int cnt = 0;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) cnt += (s[kb][r] == mx) ? 1 : 0;
-    cnt = sum32i(cnt);
+    {
+      uint32_t ma, mb, ca, cb;
+      swap_halves(__builtin_bit_cast(uint32_t, mx), ma, mb);
+      swap_halves((uint32_t)cnt, ca, cb);
+      const float fa = __builtin_bit_cast(float, ma), fb = __builtin_bit_cast(float, mb);
+      mx = fmaxf(fa, fb);
+      cnt = (fa == mx ? (int)ca : 0) + (fb == mx ? (int)cb : 0);
+    }
     if (mx == -INFINITY) cnt = 0;
     if (mx > m_run) {
       m_run = mx;
