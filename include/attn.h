@@ -30,8 +30,11 @@
  *            the kernel forms them (bf16 MFMA, fp32 accumulation); with
  *            scale > 0 this is the same order as S.
  *   Shapes   B, H, N >= 0 (B*H*N == 0 is a no-op returning ATTN_OK); any
- *            N >= 1 (ragged tiles are masked); D in {64, 128}; B*H*N*D below
- *            2^31 elements per tensor.
+ *            N >= 1 (ragged tiles are masked); D in {64, 128}; N below 2^24
+ *            and B*H*ceil(N/128) below 2^24 (one launch of 256-thread
+ *            workgroups holds fewer than 2^32 work-items).  Element offsets
+ *            are 64-bit, so a tensor may exceed 2^31 elements (4 GiB) and
+ *            the shape limits admit more than the 288 GB of one device.
  *   Ownership  The caller allocates and owns every buffer.  The library never
  *            allocates, frees or synchronises; it keeps no state between calls
  *            except a per-device cache of the device's architecture.  Inputs

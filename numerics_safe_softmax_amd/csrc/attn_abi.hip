@@ -30,12 +30,19 @@ bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u) != 0; }
 // Shape, head size, scale and beta; sets *empty when there is nothing to do.
 int check_scalars(int B, int H, int N, int D, float scale, int check_beta, float beta, bool* empty) {
   if (B < 0 || H < 0 || N < 0) return ATTN_E_SHAPE;
-  const long long rows = (long long)B * H * N;
-  if (rows * (long long)(D > 0 ? D : 1) >= (1LL << 31)) return ATTN_E_SHAPE;
+  const long long bh = (long long)B * H;
+  if (bh > 0 && N > 0) {
+    // row and key indices are 32-bit (kept well clear of overflow: N < 2^24;
+    // element offsets are 64-bit), and a launch holds fewer than 2^32
+    // work-items, i.e. fewer than 2^24 workgroups of 256 for the
+    // B * H * ceil(N / 128) row tiles of every pass
+    if (N >= (1 << 24)) return ATTN_E_SHAPE;
+    if (bh >= (1LL << 24) || bh * ((N + 127) / 128) >= (1LL << 24)) return ATTN_E_SHAPE;
+  }
   if (D != 64 && D != 128) return ATTN_E_HEADDIM;
   if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_E_SCALE;
   if (check_beta && (!std::isfinite(beta) || !(beta > 1.f))) return ATTN_E_BETA;
-  *empty = rows == 0;
+  *empty = bh == 0 || N == 0;
   return ATTN_OK;
 }
 

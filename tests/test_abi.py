@@ -75,6 +75,12 @@ def test_forward_and_backward_validation(call):
     assert call(B=-1) == -2
     assert call(N=-5) == -2
     assert call(B=1 << 14, H=1 << 14, N=1 << 10) == -2
+    assert call(N=1 << 24) == -2                       # row indices stay 32-bit
+    assert call(B=1 << 12, H=1 << 12, N=1) == -2       # 2^24 workgroups
+    assert call(B=1 << 10, H=1 << 10, N=2048) == -2    # 2^20 heads x 16 row tiles
+    # 2^31 elements per tensor is a valid shape: the call gets past the shape
+    # check and stops at the (fake, 256 MB apart) addresses' overlap instead
+    assert call(B=64, H=512, N=1024) == -7
     assert call(D=96) == -3
     assert call(D=32) == -3
     assert call(beta=1.0) == -4

@@ -8,6 +8,11 @@
   P_bar is exp(rm) < 1 and pbar_one = 0.
 * A long sequence (N = 32768, d = 128): forward parity on sampled rows, in the
   launch configuration of any other call (64-bit offsets, many KV tiles).
+* Tensors beyond 2^31 elements (4 GiB of bf16): seven seeded heads, checked
+  against the oracle, are replicated over B*H heads (head g holds head g mod 7,
+  so a 2^31-element wrap would land on a different head); forward and backward
+  on the big problem must reproduce the seven heads' outputs bit for bit in
+  every one of its heads.
 """
 import sys
 
@@ -116,3 +121,44 @@ def test_long_sequence_sampled_rows(mode):
     m.reshape(-1)[rows] = True
     fr = parity.check_forward(f, ref, rows_mask=m, label="long mode %d" % mode)
     _say("  %s" % fr)
+
+
+@pytest.mark.parametrize("D,B,H", [(64, 4, 8200), (128, 2, 8200)])
+def test_tensors_beyond_2_31_elements(D, B, H):
+    import numerics_safe_softmax_amd as nss
+    N, mode, G = 1024, 1, 7
+    assert B * H * N * D > 2 ** 31
+    w = inputs.custom("big", 1, G, N, D, True, 61 + D, tie_block=7, v_skew_dims=D // 4, v_mu=-2.0, v_sigma=0.5,
+                      do_mu=-0.5)
+    _say("beyond 2^31 elements: B=%d H=%d N=%d D=%d (%d distinct heads)" % (B, H, N, D, G))
+    d = inputs.generate(w)
+    t = parity.to_dev(d, DEV)
+    fs = parity.gpu_forward(t, w, mode)
+    bs = parity.gpu_backward(t, w, fs, mode)
+    torch.cuda.synchronize()
+    ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=True, stabilise=True, beta=w.beta)
+    rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=True)
+    parity.check_forward(fs, ref, label="seven heads")
+    parity.check_backward(bs, rb, label="seven heads")
+    idx = torch.arange(B * H, device=DEV) % G
+    big = {k: t[k][0].index_select(0, idx).view(B, H, N, D) for k in ("q", "k", "v", "dO")}
+    fb = nss.forward(big["q"], big["k"], big["v"], scale=w.scale, causal=True, stabilise=mode, beta=w.beta)
+    bb = nss.backward(big["q"], big["k"], big["v"], fb["o"], big["dO"], fb["lse"], scale=w.scale, causal=True,
+                      stabilise=mode, beta=w.beta)
+    torch.cuda.synchronize()
+    _say("  big problem done; comparing every head")
+    for name, small, large in (("o", fs["o"], fb["o"]), ("lse", fs["lse"], fb["lse"]),
+                               ("ties", fs["ties"], fb["ties"]), ("pbar_one", fs["pbar_one"], fb["pbar_one"]),
+                               ("dq", bs["dq"], bb["dq"]), ("dk", bs["dk"], bb["dk"]), ("dv", bs["dv"], bb["dv"]),
+                               ("delta", bs["delta"], bb["delta"])):
+        want = small[0].index_select(0, idx)
+        got = large.reshape(want.shape)
+        if want.dtype != torch.int32:
+            want, got = want.view(torch.int16 if want.dtype == torch.bfloat16 else torch.int32), \
+                got.view(torch.int16 if got.dtype == torch.bfloat16 else torch.int32)
+        same = (got == want).reshape(B * H, -1).all(dim=1)
+        bad = torch.nonzero(~same).flatten()
+        assert bad.numel() == 0, "%s differs in %d heads, first %s" % (name, bad.numel(), bad[:5].tolist())
+        del want, got
+    del big, fb, bb
+    torch.cuda.empty_cache()
