@@ -8,6 +8,10 @@
   P_bar is exp(rm) < 1 and pbar_one = 0.
 * A long sequence (N = 32768, d = 128): forward parity on sampled rows, in the
   launch configuration of any other call (64-bit offsets, many KV tiles).
+* Repeated maxima placed at chosen key positions: in one 32-lane half, across
+  the two halves of a 32-key block, across the two blocks of a 64-key tile,
+  across tiles, three-way, and a single maximum on the ragged last key; the
+  duplicate count must be exact whichever lanes and tiles hold the copies.
 * Tensors beyond 2^31 elements (4 GiB of bf16): seven seeded heads, checked
   against the oracle, are replicated over B*H heads (head g holds head g mod 7,
   so a 2^31-element wrap would land on a different head); forward and backward
@@ -162,3 +166,50 @@ def test_tensors_beyond_2_31_elements(D, B, H):
         del want, got
     del big, fb, bb
     torch.cuda.empty_cache()
+
+
+# key positions of the repeated maximum, one set per head (the score tile puts
+# key offset o of a 32-key block in lane half (o >> 2) & 1)
+TIE_KEYS = [(0, 4), (0, 1), (5, 32), (2, 70), (3, 4, 131), (199,)]
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_tie_positions_within_and_across_tiles(mode, D, causal):
+    import numerics_safe_softmax_amd as nss
+    rng = np.random.default_rng(500 + D + 7 * mode + int(causal))
+    H, N = len(TIE_KEYS), 200
+    q = 0.25 * rng.standard_normal((1, H, N, D))
+    q[..., 0] = 1.0
+    k = 0.25 * rng.standard_normal((1, H, N, D))
+    for h, keys in enumerate(TIE_KEYS):
+        for j in keys:
+            k[0, h, j, :] = 0.0
+            k[0, h, j, 0] = 8.0              # score 8 * scale for every row: far above the rest
+    q, k = _bits(q), _bits(k)
+    v = _bits(rng.standard_normal((1, H, N, D)))
+    dO = _bits(rng.standard_normal((1, H, N, D)))
+    t = {n: inputs.to_torch(x, DEV) for n, x in (("q", q), ("k", k), ("v", v), ("dO", dO))}
+    scale = D ** -0.5
+    f = nss.forward(t["q"], t["k"], t["v"], scale=scale, causal=causal, stabilise=mode, beta=2.0)
+    b = nss.backward(t["q"], t["k"], t["v"], f["o"], t["dO"], f["lse"], scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.forward(q, k, v, scale=scale, causal=causal, stabilise=mode != 0, beta=2.0)
+    rb = oracle.backward(q, k, v, dO, ref, scale=scale, causal=causal)
+    label = "tie keys D%d mode %d causal %d" % (D, mode, causal)
+    parity.check_forward(f, ref, label=label)
+    parity.check_backward(b, rb, label=label)
+    ties = f["ties"].cpu().numpy()[0]
+    rows = np.arange(N)
+    for h, keys in enumerate(TIE_KEYS):
+        # rows that see a copy: the count is the number of copies they see
+        want = np.array([sum(1 for j in keys if not causal or j <= i) for i in rows])
+        seen = want > 0
+        assert np.array_equal(ties[h][seen], want[seen]), (label, keys)
+        assert np.array_equal(ref["ties"][0, h][seen], want[seen])
+    if mode == 1:
+        on = oracle.online_ones(q, k, scale=scale, causal=causal, stabilise=True, beta=2.0, tile=64)
+        ok = on["amb"] == 0
+        formed = f["formed_ones"].cpu().numpy()
+        assert np.array_equal(formed[ok], on["ones"][ok]), label
