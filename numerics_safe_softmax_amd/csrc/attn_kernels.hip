@@ -38,19 +38,25 @@
 
 #include "attn_launch.h"
 
-// Tile and occupancy choices (compile-time; measured on MI355X).
+// Tile and occupancy choices (compile-time; the defaults are the variants
+// measured fastest on MI355X).
+// minimum workgroups per CU in the launch bounds of the dQ and dK/dV passes
 #ifndef NSS_DQ_WAVES
 #define NSS_DQ_WAVES 2
 #endif
 #ifndef NSS_DKDV_WAVES
 #define NSS_DKDV_WAVES 2
 #endif
+// keys per key tile of the d = 64 dQ pass
 #ifndef NSS_DQ_BN
 #define NSS_DQ_BN 64
 #endif
+// queries per query tile of the d = 64 dK/dV pass
 #ifndef NSS_DKDV_BQ
 #define NSS_DKDV_BQ 64
 #endif
+// the d = 64 dK/dV pass reads the next query block's LDS operands while the
+// current block's products run (1) or each operand where it is used (0)
 #ifndef NSS_DKDV_PF
 #define NSS_DKDV_PF 1
 #endif
