@@ -124,6 +124,46 @@ def test_tiecount_parity(case):
     assert np.allclose(rm, ref["rowmax"], rtol=2e-6, atol=1e-6)
 
 
+# rows of 2 048 keys or more: the duplicate detector (attn_tiecount and the
+# first pass of the exact-final-shift forward) streams 128-key tiles there
+LONG_ROWS = [
+    (1, 2, 2100, 64, True, 31, 20),
+    (1, 2, 2111, 64, False, 32, 0),
+    (1, 1, 3001, 128, True, 33, 25),
+    (1, 1, 2049, 128, False, 34, 0),
+]
+
+
+@pytest.mark.parametrize("case", LONG_ROWS, ids=lambda c: "B%dH%dN%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
+def test_long_row_tiecount_and_exact_shift(case):
+    import numerics_safe_softmax_amd as nss
+    w = _small_workload(*case)
+    _say("long-row detector %s" % (case,))
+    d = inputs.generate(w)
+    t = parity.to_dev(d, DEV)
+    r = nss.tiecount(t["q"], t["k"], scale=w.scale, causal=w.causal)
+    f1 = parity.gpu_forward(t, w, 1)
+    f2 = parity.gpu_forward(t, w, 2)
+    torch.cuda.synchronize()
+    ties = r["ties"].cpu().numpy()
+    # the 128-key detector and the 64-key forward form the same fp32 scores
+    assert np.array_equal(ties, f1["ties"].cpu().numpy())
+    assert np.array_equal(ties, f2["ties"].cpu().numpy())
+    ref = oracle.forward(d["q"], d["k"], scale=w.scale, causal=w.causal, want=["ties", "amb_tie", "rowmax"])
+    ok = ref["amb_tie"] == 0
+    assert np.array_equal(ties[ok], ref["ties"][ok])
+    assert np.allclose(r["rowmax"].cpu().numpy().astype(np.float64), ref["rowmax"], rtol=2e-6, atol=1e-6)
+    rng = np.random.default_rng(case[5])
+    rows = np.sort(rng.choice(w.B * w.H * w.N, 64, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, w.N - 1, w.B * w.H * w.N - 1]]))
+    m = np.zeros(w.B * w.H * w.N, dtype=bool)
+    m[rows] = True
+    ref2 = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=True, beta=w.beta,
+                          rows=rows, want=parity.FWD_WANT)
+    with parity.record_on_failure("longrow_%s" % (case,), d, w, 2):
+        parity.check_forward(f2, ref2, rows_mask=m.reshape(w.B, w.H, w.N), label="long rows %s" % (case,))
+
+
 def test_deterministic_reruns():
     w = _small_workload(2, 2, 700, 64, True, 21, 7)
     d = inputs.generate(w)
