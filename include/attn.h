@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_E_NULLPTR = -1,   /* a required pointer is NULL                          */
-  ATTN_E_SHAPE = -2,     /* B, H or N negative, or a tensor too large           */
+  ATTN_E_SHAPE = -2,     /* B, H or N negative, N >= 2^24 or B*H*ceil(N/128) >= 2^24 */
   ATTN_E_HEADDIM = -3,   /* D not in {64, 128}                                  */
   ATTN_E_BETA = -4,      /* stabilise != 0 and beta not finite or not > 1       */
   ATTN_E_SCALE = -5,     /* scale not finite or not > 0                         */
@@ -89,8 +89,10 @@ enum {
  * O = (P_bar V) / rowsum(P_bar) and LSE = m + ln rowsum(P_bar)
  * (section "机制解释二" of the same page).  The shift is applied online: while a
  * tile is processed, m comes from the running (max, count).  P_bar is formed
- * in fp32 and rounded to bf16 (nearest even) as the operand of P_bar V; the
- * row sum adds the fp32 values.
+ * in fp32 and rounded to bf16 (nearest even) as the operand of P_bar V; O is
+ * normalised by the sum of those bf16 operands (P = P_bar / rowsum(P_bar) with
+ * the P_bar that P_bar V consumes, so O's weights sum to 1), while LSE takes
+ * the sum of the fp32 values.
  *
  *   q, k, v      in   bf16 [B][H][N][D]
  *   o            out  bf16 [B][H][N][D]

@@ -92,7 +92,7 @@ const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_E_NULLPTR: return "a required pointer is NULL";
-    case ATTN_E_SHAPE: return "B, H or N negative, or a tensor of 2^31 elements or more";
+    case ATTN_E_SHAPE: return "B, H or N negative, N of 2^24 or more, or B*H*ceil(N/128) of 2^24 or more";
     case ATTN_E_HEADDIM: return "head size D must be 64 or 128";
     case ATTN_E_BETA: return "with stabilise set, beta must be finite and greater than 1";
     case ATTN_E_SCALE: return "scale must be finite and greater than 0";

@@ -130,6 +130,15 @@ __device__ __forceinline__ void wait_vmem_le() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// acc + the sum of eight bf16 values (v_dot2c_f32_bf16 against (1, 1): one
+// VALU instruction per pair, the products exact, fp32 accumulation)
+__device__ __forceinline__ float add_bf16x8(const bf16x8& p, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[e], p[e + 1]}, one, acc, false);
+  return acc;
+}
+
 // eight fp32 accumulator values -> the bf16 B operand of the next contraction.
 // SPLIT = 16: k-slice m (0 or 1) takes elements 4m..4m+3 and 8+4m..8+4m+3,
 // i.e. score rows 8m + 4h + {0..3} and 16 + 8m + 4h + {0..3} (two row quads 16
@@ -312,7 +321,10 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
   f32x16 oacc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) oacc[cb] = f32x16{};
-  float m_run = -INFINITY, m2_run = -INFINITY, lsum = 0.f;
+  // two row sums: lsum adds the fp32 P_bar (for LSE), lsum_bf the bf16 P_bar
+  // that P_bar V consumes (O's normaliser, so that O = sum_j w_j v_j with
+  // weights w_j = bf16(P_bar_j) / sum_k bf16(P_bar_k) that sum to 1)
+  float m_run = -INFINITY, m2_run = -INFINITY, lsum = 0.f, lsum_bf = 0.f;
   int c_run = 0, ones = 0;
   const bool count_ones = FORMED != nullptr;
 
@@ -389,6 +401,7 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
       const float alpha = (m2_run == -INFINITY) ? 0.f : exp2f_fast(m2_run - m2);
       m2_run = m2;
       lsum *= alpha;
+      lsum_bf *= alpha;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) oacc[cb] *= alpha;
 #pragma unroll
@@ -408,6 +421,7 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8 p0 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 0), p1 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 1);
+        lsum_bf = add_bf16x8(p1, add_bf16x8(p0, lsum_bf));
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           oacc[cb] = mfma(Tile<D, kFwdSW>::trans8(Vt, 32 * kb, 0, cb, lane), p0, oacc[cb]);
@@ -437,7 +451,7 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
   } else {
     const float ltot = sum32(lsum);
     const int ones_tot = sum32i(ones);
-    const float inv = 1.0f / ltot;
+    const float inv = 1.0f / sum32(lsum_bf);
     if (qi < N) {
       uint16_t* op = O + head + (size_t)qi * D;
 #pragma unroll
@@ -516,7 +530,7 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kern
   f32x16 oacc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) oacc[cb] = f32x16{};
-  float lsum = 0.f;
+  float lsum = 0.f, lsum_bf = 0.f;  // fp32 P_bar (LSE) and bf16 P_bar (O), as in fwd_kernel
   int ones = 0;
   const bool count_ones = FORMED != nullptr;
 
@@ -569,6 +583,7 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kern
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const bf16x8 p0 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 0), p1 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 1);
+      lsum_bf = add_bf16x8(p1, add_bf16x8(p0, lsum_bf));
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         oacc[cb] = mfma(Tile<D, kFwdSW>::trans8(Vt, 32 * kb, 0, cb, lane), p0, oacc[cb]);
@@ -584,7 +599,7 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kern
   if (qw >= N) return;
   const float ltot = sum32(lsum);
   const int ones_tot = sum32i(ones);
-  const float inv = 1.0f / ltot;
+  const float inv = 1.0f / sum32(lsum_bf);
   if (qi >= N) return;
   uint16_t* op = O + head + (size_t)qi * D;
 #pragma unroll

@@ -42,6 +42,9 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -9, -10):
         assert binding.status_string(s) and binding.status_string(s) != "unknown attn_status"
     assert binding.status_string(12345) == "unknown attn_status"
+    # the shape status names the limits the check enforces (N and the launch grid)
+    shape_text = binding.status_string(-2)
+    assert "2^24" in shape_text and "ceil(N/128)" in shape_text and "2^31" not in shape_text
     assert binding.abi_version() == 3
 
 

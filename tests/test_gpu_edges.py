@@ -213,3 +213,87 @@ def test_tie_positions_within_and_across_tiles(mode, D, causal):
         ok = on["amb"] == 0
         formed = f["formed_ones"].cpu().numpy()
         assert np.array_equal(formed[ok], on["ones"][ok]), label
+
+
+# The online rule's rescale can grow (itsolotime.com/archives/23922, section
+# 极简修复方案, applied to the running (max, count) pair): a maximum repeated
+# in an early KV tile moves the shift to beta * rm (rm > 0) or to 0 (rm < 0);
+# a later, larger single maximum that stays below beta * rm (or below 0)
+# brings the shift back down to itself, so the rescale factor
+# alpha = exp(shift_old - shift_new) exceeds 1.  Per head: the repeated keys,
+# their raw score, the overtaking key and its raw score (q_i = e_0 plus a
+# small second component, so the marked keys score exactly their value).
+R10_HEADS = [
+    ((10, 40), 4.0, 150, 6.0),     # positive: shift 8 -> 6 (alpha = e^(2 scale))
+    ((10, 70), 4.0, 150, 7.5),     # the repeat completes in tile 1 (shift up), then down in tile 2
+    ((10, 40), -1.0, 150, -0.5),   # negative: shift 0 -> -0.5
+    ((3, 60), -2.0, 100, -1.25),   # negative, overtaken in the next tile
+]
+
+
+def _online_shifts(raw, beta, tile):
+    """The rule's shift after each tile of one row (exact small numbers)."""
+    out, m, c = [], -np.inf, 0
+    for t0 in range(0, len(raw), tile):
+        seg = raw[t0:t0 + tile]
+        mx = max(seg)
+        cnt = sum(1 for x in seg if x == mx)
+        if mx > m:
+            m, c = mx, cnt
+        elif mx == m:
+            c += cnt
+        out.append(beta * m if c > 1 and m > 0 else (0.0 if c > 1 and m < 0 else m))
+    return out
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_shift_moves_down(mode, D, causal):
+    import numerics_safe_softmax_amd as nss
+    rng = np.random.default_rng(700 + D + 3 * mode + int(causal))
+    H, N, beta = len(R10_HEADS), 200, 2.0
+    q = np.zeros((1, H, N, D))
+    q[..., 0] = 1.0
+    q[..., 1] = 0.25 * rng.standard_normal((1, H, N))
+    k = np.zeros((1, H, N, D))
+    k[..., 1] = 0.25 * rng.standard_normal((1, H, N))
+    for h, (reps, a, b, bval) in enumerate(R10_HEADS):
+        # the other keys score well below the marked ones
+        low = min(a, bval) - 3.0
+        k[0, h, :, 0] = low - 0.25 * np.abs(rng.standard_normal(N))
+        for j in reps:
+            k[0, h, j, :2] = (a, 0.0)
+        k[0, h, b, :2] = (bval, 0.0)
+    q, k = _bits(q), _bits(k)
+    v = rng.standard_normal((1, H, N, D))
+    v[..., :16] = -2.0 + 0.5 * rng.standard_normal((1, H, N, 16))
+    v, dO = _bits(v), _bits(rng.standard_normal((1, H, N, D)))
+    scale = D ** -0.5
+    # the construction: on the rows that see every marked key the running shift
+    # rises at the repeat and falls at the overtaking key
+    for h, (reps, a, b, bval) in enumerate(R10_HEADS):
+        raw = inputs.bits_to_float(k[0, h, :, 0]).astype(np.float64)
+        sh = _online_shifts(list(raw), beta, 64)
+        assert sh[b // 64] < sh[b // 64 - 1], (h, sh)
+    t = {n: inputs.to_torch(x, DEV) for n, x in (("q", q), ("k", k), ("v", v), ("dO", dO))}
+    label = "shift moves down D%d mode %d causal %d" % (D, mode, causal)
+    _say(label)
+    f = nss.forward(t["q"], t["k"], t["v"], scale=scale, causal=causal, stabilise=mode, beta=beta)
+    b = nss.backward(t["q"], t["k"], t["v"], f["o"], t["dO"], f["lse"], scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.forward(q, k, v, scale=scale, causal=causal, stabilise=mode != 0, beta=beta)
+    rb = oracle.backward(q, k, v, dO, ref, scale=scale, causal=causal)
+    parity.check_forward(f, ref, label=label)
+    parity.check_backward(b, rb, label=label)
+    ties = f["ties"].cpu().numpy()[0]
+    for h, (reps, a, bkey, bval) in enumerate(R10_HEADS):
+        seen_b = np.arange(N) >= bkey if causal else np.ones(N, dtype=bool)
+        assert np.all(ties[h][seen_b] == 1), label          # the overtaking key is the single maximum
+    if mode in (0, 1):
+        on = oracle.online_ones(q, k, scale=scale, causal=causal, stabilise=mode == 1, beta=beta, tile=64)
+        ok = on["amb"] == 0
+        assert np.array_equal(f["formed_ones"].cpu().numpy()[ok], on["ones"][ok]), label
+    else:
+        exn = (ref["amb_tie"] == 0) & (ref["amb_near"] == 0)
+        assert np.array_equal(f["formed_ones"].cpu().numpy()[exn], ref["near_ones"][exn]), label
