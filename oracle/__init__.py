@@ -20,7 +20,10 @@ Low-Precision Transformer Training Fails: An Analysis on Flash Attention"):
 
 Parity status of every function is pinned by ``tests/test_oracle_*.py``
 (closed forms, brute force, identities, finite differences, the worked
-example); nothing here is "parity unpinned".
+example); the tolerance tensors by ``tests/test_oracle_tolerance.py`` (an
+independent model of the kernels' arithmetic lands inside them, planted
+mistakes land outside); the bias statistics of ``bias.py`` by
+``tests/test_bias_stats.py``.  Nothing here is "parity unpinned".
 """
 from __future__ import annotations
 

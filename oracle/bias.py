@@ -12,6 +12,11 @@ negatively skewed V dimensions, the mean signed error of O in bf16 ulps of the
 reference, and of delta in units of u * sum_c |dO_ic O_ic| (u = 2^-8), with a
 row-clustered standard error (each row's mean is one sample) and z = mean/SEM.
 Controls: rows without a repeat, and the other dimensions.
+
+Pinned by tests/test_bias_stats.py: ulp_bf16 against the exhaustive bf16
+grid, the statistics against constructed errors of known mean and
+row-clustered spread, event_curve against a hand-built event array, and the
+whole report against the row-sum reading on the sink workload.
 """
 from __future__ import annotations
 

@@ -343,6 +343,7 @@ static inline int last_key(const orc_problem* p, int i) { return p->causal ? i :
 typedef struct {
   double* raw;    /* [N] exact q.k */
   double* sabs;   /* [N] sum |q_c k_c| */
+  double* err;    /* [N] relative error bound of the kernel's P_bar_j beyond its bf16 rounding */
   int* f32exact;  /* [N] every fp32 partial sum exact */
   char* ismax;    /* [N] raw_j equals the row max exactly */
   kacc* ka;       /* [N] exact accumulators (only when needed) */
@@ -351,12 +352,13 @@ typedef struct {
 static void scratch_init(row_scratch* s, int N) {
   s->raw = (double*)malloc(sizeof(double) * (size_t)N);
   s->sabs = (double*)malloc(sizeof(double) * (size_t)N);
+  s->err = (double*)malloc(sizeof(double) * (size_t)N);
   s->f32exact = (int*)malloc(sizeof(int) * (size_t)N);
   s->ismax = (char*)malloc((size_t)N);
   s->ka = NULL;
 }
 static void scratch_free(row_scratch* s) {
-  free(s->raw); free(s->sabs); free(s->f32exact); free(s->ismax); free(s->ka);
+  free(s->raw); free(s->sabs); free(s->err); free(s->f32exact); free(s->ismax); free(s->ka);
 }
 
 /*
@@ -485,10 +487,27 @@ static void forward_row(const orc_problem* p, const decoded* dc, int64_t row, ro
   const double pmax = exp(rm - mstar);
   const double nfac = (double)nvis * U_F32;
 
+  /*
+   * Error of the kernel's P_bar_j beyond its bf16 rounding, as a relative
+   * error (natural-log units of its exponent): the fp32 dot product (at most
+   * D fp32 additions of exact bf16 products), the rounding of scale * log2(e)
+   * and of the exponent (at most |S_j| + |shift| in size, for any shift the
+   * online rule passes through), and exp2 itself.
+   */
+  const double shift_mag = fabs(rm) * (1.0 + (p->stabilise ? p->beta : 0.0));
+  double lse_score = 0.0;  /* sum_j P_j * that error: its effect on LSE */
+  for (int j = 0; j <= jl; ++j) {
+    const double sj = p->scale * s->raw[j];
+    const double ej = p->scale * D * U_F32 * s->sabs[j] + 0x1p-22 * (2.0 * fabs(sj) + shift_mag + 1.0);
+    s->err[j] = ej;
+    lse_score += exp(sj - rm) / ell * ej;
+  }
+
   if (out->O || out->tol_O || out->O_stab) {
     double* o = (double*)calloc((size_t)D, sizeof(double));
     double* oa = (double*)calloc((size_t)D, sizeof(double));
     double* os = (double*)calloc((size_t)D, sizeof(double));
+    double* dev = (double*)calloc((size_t)D, sizeof(double));
     for (int j = 0; j <= jl; ++j) {
       double sj = p->scale * s->raw[j];
       double pj = exp(sj - rm) / ell;
@@ -500,19 +519,42 @@ static void forward_row(const orc_problem* p, const decoded* dc, int64_t row, ro
         os[c] += pbj * vj[c];
       }
     }
+    if (out->tol_O) {
+      /*
+       * O = sum_j w_j v_j with w_j = p_j / sum_k p_k, p_j = P_bar_j (1 + e_j):
+       * normalising by the sum of the very values that multiply V gives
+       * O' - O = sum_j P_j e_j (v_j - O) / (1 + sum_k P_k e_k), so a relative
+       * error e_j of each weight (u from the bf16 rounding of P_bar, plus the
+       * score error above) is bounded by sum_j P_j |e_j| |v_j - O|.
+       */
+      for (int j = 0; j <= jl; ++j) {
+        const double w = exp(p->scale * s->raw[j] - rm) / ell * (U_BF16 + s->err[j]);
+        const double* vj = dc->v + (bh * N + j) * D;
+        for (int c = 0; c < D; ++c) dev[c] += w * fabs(vj[c] - o[c]);
+      }
+    }
     const int64_t base = row * D;
     for (int c = 0; c < D; ++c) {
       if (out->O) out->O[base + c] = o[c];
       if (out->O_stab) out->O_stab[base + c] = ell_stab > 0.0 ? os[c] : NAN;
-      /* bf16 P_bar operand (2u per term), bf16 output (u), fp32 sums over the row */
+      /* the weights' errors, the bf16 output (u), fp32 sums over the row; x2 */
       if (out->tol_O)
-        out->tol_O[base + c] = 2.0 * (2.0 * U_BF16 * oa[c] + U_BF16 * fabs(o[c])) +
-                               2.0 * nfac * (oa[c] + fabs(o[c]));
+        out->tol_O[base + c] = 2.0 * (dev[c] + U_BF16 * fabs(o[c])) + 2.0 * nfac * (oa[c] + fabs(o[c]));
     }
-    free(o); free(oa); free(os);
+    free(o); free(oa); free(os); free(dev);
   }
   if (out->lse) out->lse[row] = lse;
-  if (out->tol_lse) out->tol_lse[row] = 1e-5 + 2.0 * nfac + 0x1p-22 * fabs(lse);
+  /*
+   * LSE = (shift + log2 l) ln 2 with l the fp32 sum of the row's P_bar: each
+   * lane adds half the row's keys one by one and rescales once per 64-key
+   * tile (relative error (n/2 + n/64 + 2) 2^-24 of a sum of positive terms);
+   * the weights' score errors move LSE by sum_j P_j e_j; log2 and the final
+   * sum and product round once each.  x2.
+   */
+  if (out->tol_lse)
+    out->tol_lse[row] = 2.0 * (lse_score + ((double)nvis / 2.0 + (double)nvis / 64.0 + 2.0) * U_F32 +
+                               0x1p-22 * log(2.0) * fmax(1.0, fabs(lse - mstar) / log(2.0)) +
+                               0x1p-23 * fabs(lse));
   if (out->rowmax) out->rowmax[row] = rm;
   if (out->shift) out->shift[row] = mstar;
   if (out->pbar_max) out->pbar_max[row] = pmax;
@@ -736,6 +778,7 @@ int orc_backward(const orc_problem* p, const int64_t* heads, int64_t nheads, con
                  const orc_bwd_out* out) {
   if (p->N <= 0 || p->B <= 0 || p->H <= 0) return 0;
   if (!p->dO || !O || !lse || !tol_O || !tol_lse) return -1;
+  (void)tol_O; /* delta's bound follows the forward's error model directly (below) */
   decoded dc;
   if (decode_problem(p, &dc) != 0) { free_decoded(&dc); return -1; }
   const int N = p->N, D = p->D;
@@ -746,59 +789,100 @@ int orc_backward(const orc_problem* p, const int64_t* heads, int64_t nheads, con
   double* delta = (double*)malloc(sizeof(double) * (size_t)p->B * p->H * N);
   double* tdel = (double*)malloc(sizeof(double) * (size_t)p->B * p->H * N);
 
+  /*
+   * Error model of a bf16 kernel with fp32 accumulation (x2 in every
+   * tolerance).  e_b(i, j): relative error of the kernel's P_ij = exp(S_ij -
+   * LSE_i) beyond the LSE's own error: the fp32 dot product (D additions of
+   * exact bf16 products), the rounding of scale * log2(e), of the exponent and
+   * of LSE * log2(e), and exp2.  The forward's O reaches delta through
+   * delta_i = sum_c dO_ic O_ic: with O' - O = sum_j P_ij e_j (v_j - O) plus
+   * the rounding r_c of each bf16 output, the error of delta is
+   * sum_j P_ij e_j (dP_ij - delta_i) + sum_c dO_ic r_c, so it is bounded by
+   * sum_j P_ij |e_j| |dP_ij - delta_i| + u sum_c |dO_ic O_ic| (e_j: u for the
+   * bf16 P_bar plus the forward's score error), plus the fp32 sums of the
+   * forward (n 2^-24 per term) and of delta itself (D 2^-24).
+   */
   /* pass 1, per query row: delta, then dQ = scale * sum_j dS_ij k_j */
 #pragma omp parallel
   {
     double* acc = (double*)malloc(sizeof(double) * (size_t)D);
     double* tac = (double*)malloc(sizeof(double) * (size_t)D);
+    double* pk = (double*)malloc(sizeof(double) * (size_t)D);
+    double* Pj = (double*)malloc(sizeof(double) * (size_t)N);
+    double* dpj = (double*)malloc(sizeof(double) * (size_t)N);
+    double* dpaj = (double*)malloc(sizeof(double) * (size_t)N);
+    double* sj = (double*)malloc(sizeof(double) * (size_t)N);
+    double* saj = (double*)malloc(sizeof(double) * (size_t)N);
 #pragma omp for schedule(dynamic, 8)
     for (int64_t t = 0; t < total; ++t) {
       const int64_t bh = heads ? heads[t / N] : t / N;
       const int i = (int)(t % N);
       const int64_t row = bh * N + i;
       const double* o = O + row * D;
-      const double* to = tol_O + row * D;
       const double* g = dc.dO + row * D;
       const double* q = dc.q + row * D;
-      double dl = 0.0, dla = 0.0, dlt = 0.0;
+      double dl = 0.0, dla = 0.0;
       for (int c = 0; c < D; ++c) {
         dl += g[c] * o[c];
         dla += fabs(g[c] * o[c]);
-        dlt += fabs(g[c]) * to[c];
       }
-      const double td = 2.0 * dlt + gamma * dla;
-      delta[row] = dl;
-      tdel[row] = td;
-      for (int c = 0; c < D; ++c) { acc[c] = 0.0; tac[c] = 0.0; }
       const int jl = last_key(p, i);
+      const int nvis = jl + 1;
+      double rm = -INFINITY;
       for (int j = 0; j <= jl; ++j) {
         const int64_t kr = bh * N + j;
         const double* k = dc.k + kr * D;
         const double* v = dc.v + kr * D;
-        double raw = 0.0, dp = 0.0, dpa = 0.0;
+        double raw = 0.0, sa = 0.0, dp = 0.0, dpa = 0.0;
         for (int c = 0; c < D; ++c) {
           raw += q[c] * k[c];
+          sa += fabs(q[c] * k[c]);
           dp += g[c] * v[c];
           dpa += fabs(g[c] * v[c]);
         }
-        const double P = exp(sc * raw - lse[row]);
-        const double dS = P * (dp - dl);
-        const double eds = U_BF16 * fabs(dS) + P * (td + gamma * dpa) +
-                           fabs(dS) * (tol_lse[row] + 0x1p-18);
+        sj[j] = sc * raw;
+        saj[j] = sa;
+        dpj[j] = dp;
+        dpaj[j] = dpa;
+        Pj[j] = exp(sc * raw - lse[row]);
+        if (sj[j] > rm) rm = sj[j];
+      }
+      /* the forward's shift is at most |rm| (1 + beta) in size, whichever mode */
+      const double shift_mag = fabs(rm) * (1.0 + (p->stabilise ? p->beta : 0.0));
+      double dev = 0.0, pdpa = 0.0;
+      for (int j = 0; j <= jl; ++j) {
+        const double ef = sc * D * U_F32 * saj[j] + 0x1p-22 * (2.0 * fabs(sj[j]) + shift_mag + 1.0);
+        dev += Pj[j] * (U_BF16 + ef) * fabs(dpj[j] - dl);
+        pdpa += Pj[j] * dpaj[j];
+      }
+      const double nfac = (double)nvis * U_F32;
+      const double td = 2.0 * (dev + U_BF16 * dla + nfac * (pdpa + dla)) + gamma * dla;
+      delta[row] = dl;
+      tdel[row] = td;
+      for (int c = 0; c < D; ++c) { acc[c] = 0.0; tac[c] = 0.0; pk[c] = 0.0; }
+      for (int j = 0; j <= jl; ++j) {
+        const double* k = dc.k + (bh * N + j) * D;
+        const double P = Pj[j];
+        const double dS = P * (dpj[j] - dl);
+        const double eb = tol_lse[row] + sc * D * U_F32 * saj[j] + 0x1p-22 * (2.0 * fabs(sj[j]) + fabs(lse[row]) + 1.0);
+        /* per-entry errors of dS; delta's error, common to the row, is added below */
+        const double eds = U_BF16 * fabs(dS) + P * gamma * dpaj[j] + (fabs(dS) + P * td) * eb;
         for (int c = 0; c < D; ++c) {
           acc[c] += dS * k[c];
           tac[c] += eds * fabs(k[c]);
+          pk[c] += P * k[c];
         }
       }
       for (int c = 0; c < D; ++c) {
         const double dq = sc * acc[c];
         if (out->dQ) out->dQ[row * D + c] = dq;
-        if (out->tol_dQ) out->tol_dQ[row * D + c] = 2.0 * (sc * tac[c] + U_BF16 * fabs(dq));
+        /* delta's error d enters dQ_i as -scale d sum_j P_ij k_j */
+        if (out->tol_dQ) out->tol_dQ[row * D + c] = 2.0 * (sc * (tac[c] + td * fabs(pk[c])) + U_BF16 * fabs(dq));
       }
       if (out->delta) out->delta[row] = dl;
       if (out->tol_delta) out->tol_delta[row] = td;
     }
-    free(acc); free(tac);
+    free(acc); free(tac); free(pk); free(Pj); free(dpj); free(dpaj); free(sj); free(saj);
   }
 
   /* pass 2, per key row: dK = scale * sum_i dS_ij q_i, dV = sum_i P_ij dO_i */
@@ -821,17 +905,19 @@ int orc_backward(const orc_problem* p, const int64_t* heads, int64_t nheads, con
         const int64_t row = bh * N + i;
         const double* q = dc.q + row * D;
         const double* g = dc.dO + row * D;
-        double raw = 0.0, dp = 0.0, dpa = 0.0;
+        double raw = 0.0, sa = 0.0, dp = 0.0, dpa = 0.0;
         for (int c = 0; c < D; ++c) {
           raw += q[c] * k[c];
+          sa += fabs(q[c] * k[c]);
           dp += g[c] * v[c];
           dpa += fabs(g[c] * v[c]);
         }
         const double P = exp(sc * raw - lse[row]);
         const double dS = P * (dp - delta[row]);
-        const double eds = U_BF16 * fabs(dS) + P * (tdel[row] + gamma * dpa) +
-                           fabs(dS) * (tol_lse[row] + 0x1p-18);
-        const double ep = P * (tol_lse[row] + 0x1p-18);
+        const double eb = tol_lse[row] + sc * D * U_F32 * sa + 0x1p-22 * (2.0 * fabs(sc * raw) + fabs(lse[row]) + 1.0);
+        /* delta's error differs from row to row here: bounded term by term */
+        const double eds = U_BF16 * fabs(dS) + P * (tdel[row] + gamma * dpa) + (fabs(dS) + P * tdel[row]) * eb;
+        const double ep = P * eb;
         for (int c = 0; c < D; ++c) {
           ak[c] += dS * q[c];
           tk[c] += eds * fabs(q[c]);
