@@ -66,6 +66,7 @@ typedef enum {
   ATTN_E_SCALE = -5,     /* scale not finite or not > 0                         */
   ATTN_E_ALIGN = -6,     /* a pointer is not 16-byte aligned                    */
   ATTN_E_ALIAS = -7,     /* an output overlaps an input or another output       */
+  ATTN_E_WORKSPACE = -8, /* workspace smaller than attn_bwd_workspace_bytes, or misaligned */
   ATTN_E_DEVICE = -9,    /* not a gfx950 device, or a HIP launch failed         */
   ATTN_E_MODE = -10      /* stabilise not 0, 1 or 2                             */
 } attn_status;
@@ -149,22 +150,39 @@ int attn_fwd_o32(const void* q, const void* k, const void* v, void* o, float* o3
                  float beta, void* stream);
 
 /*
+ * attn_bwd_workspace_bytes -- size of the workspace attn_bwd needs: 0 for
+ * every shape.  The backward keeps every intermediate in registers and LDS
+ * (two passes: attn_bwd_dq then attn_bwd_dkdv; a one-pass form with dQ added
+ * into an fp32 workspace by atomics measured slower on MI355X).  The query and
+ * the workspace arguments are part of the interface so that a caller that
+ * sizes the workspace by this call is correct whatever it returns.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int D);
+
+/*
  * attn_bwd -- gradient of sum(dO * O) with respect to q, k and v.
  *
  * Runs attn_bwd_dq then attn_bwd_dkdv on `stream`.  With P = exp(S - lse):
- * delta_i = sum_c dO_ic O_ic (91haoming.cn/news/show-608006, section 三),
- * dP = dO V^T, dS = P o (dP - delta), dQ = scale dS K, dK = scale dS^T Q,
- * dV = P^T dO.  P is recomputed from the forward's lse, which carries the
- * forward's shift, so the arithmetic is the same in every mode; `stabilise`
- * and `beta` are validated as for attn_fwd and otherwise unused.
+ * delta_i = sum_c dO_ic O_ic (91haoming.cn/news/show-608006, section 三: a
+ * row-sum of an element-wise product), dP = dO V^T, dS = P o (dP - delta),
+ * dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.  P is recomputed from the
+ * forward's lse, which carries the forward's shift, so the arithmetic is the
+ * same in every mode; `stabilise` and `beta` are validated as for attn_fwd
+ * and otherwise unused.  Every output is reproducible bit for bit.
  *
  *   q, k, v, o, dO  in   bf16 [B][H][N][D] (o from attn_fwd)
  *   lse             in   fp32 [B][H][N] from attn_fwd
  *   dq, dk, dv      out  bf16 [B][H][N][D]
  *   delta           out  fp32 [B][H][N]: rowsum(dO o O), kept for the caller
+ *   workspace       at least attn_bwd_workspace_bytes(B, H, N, D) bytes of
+ *                   caller-owned device scratch, 16-byte aligned, contents
+ *                   undefined on entry and on exit (NULL with 0 bytes where
+ *                   that size is 0, as it is for every shape here); a
+ *                   smaller or misaligned one is ATTN_E_WORKSPACE
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
              const float* lse, void* dq, void* dk, void* dv, float* delta,
+             void* workspace, size_t workspace_bytes,
              int B, int H, int N, int D, float scale, int causal, int stabilise,
              float beta, void* stream);
 
@@ -177,19 +195,20 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  */
 int attn_bwd_o32(const void* q, const void* k, const void* v, const float* o32, const void* dO,
                  const float* lse, void* dq, void* dk, void* dv, float* delta,
+                 void* workspace, size_t workspace_bytes,
                  int B, int H, int N, int D, float scale, int causal, int stabilise,
                  float beta, void* stream);
 
 /*
- * attn_bwd_dq -- first half of attn_bwd: delta and dQ, one pass per query
- * tile over its visible keys.  Arguments as attn_bwd.
+ * attn_bwd_dq -- first pass of attn_bwd: delta and dQ, one pass per query
+ * tile over its visible keys (recomputing S and dP).  Arguments as attn_bwd.
  */
 int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
                 const float* lse, void* dq, float* delta,
                 int B, int H, int N, int D, float scale, int causal, void* stream);
 
 /*
- * attn_bwd_dkdv -- second half of attn_bwd: dK and dV, one pass per key tile
+ * attn_bwd_dkdv -- second pass of attn_bwd: dK and dV, one pass per key tile
  * over the queries that see it.  `delta` is read (attn_bwd_dq's output).
  */
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,

@@ -20,12 +20,14 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "attn.h")
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
+_Z = ctypes.c_size_t
 
 _SIGS = {
     "attn_fwd": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _F, _P],
     "attn_fwd_o32": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _F, _P],
-    "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _F, _P],
-    "attn_bwd_o32": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _F, _P],
+    "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _F, _I, _I, _F, _P],
+    "attn_bwd_o32": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _F, _I, _I, _F, _P],
+    "attn_bwd_workspace_bytes": [_I, _I, _I, _I],
     "attn_bwd_dq": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P],
     "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P],
     "attn_tiecount": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P],
@@ -53,7 +55,8 @@ def lib():
         for name, args in _SIGS.items():
             f = getattr(L, name)
             f.argtypes = args
-            f.restype = ctypes.c_char_p if name == "attn_status_string" else ctypes.c_int
+            f.restype = {"attn_status_string": ctypes.c_char_p,
+                         "attn_bwd_workspace_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
         _lib = L
     return _lib
 
@@ -157,23 +160,36 @@ def attn_fwd_o32(q, k, v, o, o32, lse, ties=None, pbar_one=None, formed_ones=Non
                               _mode(stabilise), float(beta), _stream(stream)))
 
 
-def attn_bwd_o32(q, k, v, o32, dO, lse, dq, dk, dv, delta, *, scale: float, causal: bool, stabilise: bool,
-                 beta: float = 2.0, stream=None) -> None:
+def attn_bwd_workspace_bytes(B: int, H: int, N: int, D: int) -> int:
+    return int(lib().attn_bwd_workspace_bytes(int(B), int(H), int(N), int(D)))
+
+
+def _ws(workspace):
+    """(pointer, bytes) of a workspace tensor (any dtype, on the GPU), or (None, 0)."""
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def attn_bwd_o32(q, k, v, o32, dO, lse, dq, dk, dv, delta, workspace=None, *, scale: float, causal: bool,
+                 stabilise: bool, beta: float = 2.0, stream=None) -> None:
     import torch
     B, H, N, D = _check_args(q, mats=(("k", k), ("v", v), ("dO", dO), ("dq", dq), ("dk", dk), ("dv", dv)),
                              rows=(("lse", lse), ("delta", delta)))
     _expect(o32, torch.float32, (B, H, N, D), "o32")
+    wp, wb = _ws(workspace)
     _check(lib().attn_bwd_o32(_ptr(q), _ptr(k), _ptr(v), _ptr(o32), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
-                              _ptr(dv), _ptr(delta), B, H, N, D, float(scale), int(bool(causal)),
+                              _ptr(dv), _ptr(delta), wp, wb, B, H, N, D, float(scale), int(bool(causal)),
                               _mode(stabilise), float(beta), _stream(stream)))
 
 
-def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, *, scale: float, causal: bool, stabilise: bool,
-             beta: float = 2.0, stream=None) -> None:
+def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, workspace=None, *, scale: float, causal: bool,
+             stabilise: bool, beta: float = 2.0, stream=None) -> None:
     B, H, N, D = _check_args(q, mats=(("k", k), ("v", v), ("o", o), ("dO", dO), ("dq", dq), ("dk", dk),
                                       ("dv", dv)), rows=(("lse", lse), ("delta", delta)))
+    wp, wb = _ws(workspace)
     _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
-                          _ptr(dv), _ptr(delta), B, H, N, D, float(scale), int(bool(causal)),
+                          _ptr(dv), _ptr(delta), wp, wb, B, H, N, D, float(scale), int(bool(causal)),
                           _mode(stabilise), float(beta), _stream(stream)))
 
 
@@ -221,18 +237,27 @@ def forward(q, k, v, *, scale: float, causal: bool, stabilise: bool, beta: float
     return out
 
 
+def workspace_for(q):
+    """A workspace tensor of attn_bwd_workspace_bytes for q's shape (None when 0)."""
+    import torch
+    nb = attn_bwd_workspace_bytes(*_shape(q))
+    return torch.empty(nb // 4, dtype=torch.float32, device=q.device) if nb else None
+
+
 def backward(q, k, v, o, dO, lse, *, scale: float, causal: bool, stabilise: bool = False,
-             beta: float = 2.0, o32=None, stream=None) -> dict:
-    """attn_bwd (or attn_bwd_o32 when the fp32 O is given: delta from it)."""
+             beta: float = 2.0, o32=None, workspace=None, stream=None) -> dict:
+    """attn_bwd (or attn_bwd_o32 when the fp32 O is given: delta from it); the
+    workspace is allocated here unless one is passed."""
     import torch
     B, H, N, D = _shape(q)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(q), "dv": torch.empty_like(q),
            "delta": torch.empty((B, H, N), dtype=torch.float32, device=q.device)}
+    ws = workspace if workspace is not None else workspace_for(q)
     if o32 is not None:
-        attn_bwd_o32(q, k, v, o32, dO, lse, out["dq"], out["dk"], out["dv"], out["delta"], scale=scale,
+        attn_bwd_o32(q, k, v, o32, dO, lse, out["dq"], out["dk"], out["dv"], out["delta"], ws, scale=scale,
                      causal=causal, stabilise=stabilise, beta=beta, stream=stream)
     else:
-        attn_bwd(q, k, v, o, dO, lse, out["dq"], out["dk"], out["dv"], out["delta"], scale=scale,
+        attn_bwd(q, k, v, o, dO, lse, out["dq"], out["dk"], out["dv"], out["delta"], ws, scale=scale,
                  causal=causal, stabilise=stabilise, beta=beta, stream=stream)
     return out
 

@@ -86,7 +86,7 @@ int launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_DEVICE; }
 
 extern "C" {
 
-int attn_abi_version(void) { return 3; }
+int attn_abi_version(void) { return 4; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -98,6 +98,7 @@ const char* attn_status_string(int status) {
     case ATTN_E_SCALE: return "scale must be finite and greater than 0";
     case ATTN_E_ALIGN: return "every pointer must be 16-byte aligned";
     case ATTN_E_ALIAS: return "an output overlaps an input or another output";
+    case ATTN_E_WORKSPACE: return "workspace is NULL, misaligned or smaller than attn_bwd_workspace_bytes";
     case ATTN_E_DEVICE: return "not a gfx950 device, or a HIP launch failed";
     case ATTN_E_MODE: return "stabilise must be 0 (plain), 1 (online shift) or 2 (exact final shift)";
     default: return "unknown attn_status";
@@ -198,44 +199,51 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, c
   return launched(nss::launch_bwd_dkdv(a, (hipStream_t)stream));
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
-             void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int D, float scale, int causal,
-             int stabilise, float beta, void* stream) {
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int D) {
+  (void)B; (void)H; (void)N; (void)D;
+  return 0;  // the two-pass backward keeps everything in registers and LDS
+}
+
+namespace {
+
+// validation shared by attn_bwd and attn_bwd_o32 (o: bf16 O, or fp32 O when o32)
+int bwd_entry(const void* q, const void* k, const void* v, const void* o, bool o32, const void* dO,
+              const float* lse, void* dq, void* dk, void* dv, float* delta, void* workspace, size_t workspace_bytes,
+              int B, int H, int N, int D, float scale, int causal, int stabilise, float beta, void* stream) {
   bool empty = false;
   int st = check_scalars(B, H, N, D, scale, stabilise != 0, beta, &empty);
   if (st == ATTN_OK && (stabilise < 0 || stabilise > 2)) st = ATTN_E_MODE;
   if (st != ATTN_OK || empty) return st;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !delta) return ATTN_E_NULLPTR;
+  const size_t need = attn_bwd_workspace_bytes(B, H, N, D);
+  if (need && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u) != 0)) return ATTN_E_WORKSPACE;
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv, delta};
   if ((st = check_align(ptrs, 10)) != ATTN_OK) return st;
   const size_t tb = (size_t)B * H * N * D * 2, rb = (size_t)B * H * N * 4;
-  const Span in[] = {{q, tb}, {k, tb}, {v, tb}, {o, tb}, {dO, tb}, {lse, rb}};
+  const Span in[] = {{q, tb}, {k, tb}, {v, tb}, {o, o32 ? 2 * tb : tb}, {dO, tb}, {lse, rb}};
   const Span out[] = {{dq, tb}, {dk, tb}, {dv, tb}, {delta, rb}};
   if ((st = check_alias(in, 6, out, 4)) != ATTN_OK) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  nss::BwdArgs a{q, k, v, o, dO, nullptr, lse, dq, dk, dv, delta, B, H, N, D, scale, causal ? 1 : 0};
+  nss::BwdArgs a{q, k, v, o32 ? nullptr : o, dO, o32 ? static_cast<const float*>(o) : nullptr, lse, dq, dk, dv,
+                 delta, B, H, N, D, scale, causal ? 1 : 0};
   if ((st = launched(nss::launch_bwd_dq(a, (hipStream_t)stream))) != ATTN_OK) return st;
   return launched(nss::launch_bwd_dkdv(a, (hipStream_t)stream));
 }
 
+}  // namespace
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             void* dq, void* dk, void* dv, float* delta, void* workspace, size_t workspace_bytes, int B, int H, int N,
+             int D, float scale, int causal, int stabilise, float beta, void* stream) {
+  return bwd_entry(q, k, v, o, false, dO, lse, dq, dk, dv, delta, workspace, workspace_bytes, B, H, N, D, scale,
+                   causal, stabilise, beta, stream);
+}
+
 int attn_bwd_o32(const void* q, const void* k, const void* v, const float* o32, const void* dO, const float* lse,
-                 void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int D, float scale, int causal,
-                 int stabilise, float beta, void* stream) {
-  bool empty = false;
-  int st = check_scalars(B, H, N, D, scale, stabilise != 0, beta, &empty);
-  if (st == ATTN_OK && (stabilise < 0 || stabilise > 2)) st = ATTN_E_MODE;
-  if (st != ATTN_OK || empty) return st;
-  if (!q || !k || !v || !o32 || !dO || !lse || !dq || !dk || !dv || !delta) return ATTN_E_NULLPTR;
-  const void* ptrs[] = {q, k, v, o32, dO, lse, dq, dk, dv, delta};
-  if ((st = check_align(ptrs, 10)) != ATTN_OK) return st;
-  const size_t tb = (size_t)B * H * N * D * 2, rb = (size_t)B * H * N * 4;
-  const Span in[] = {{q, tb}, {k, tb}, {v, tb}, {o32, 2 * tb}, {dO, tb}, {lse, rb}};
-  const Span out[] = {{dq, tb}, {dk, tb}, {dv, tb}, {delta, rb}};
-  if ((st = check_alias(in, 6, out, 4)) != ATTN_OK) return st;
-  if ((st = check_device()) != ATTN_OK) return st;
-  nss::BwdArgs a{q, k, v, nullptr, dO, o32, lse, dq, dk, dv, delta, B, H, N, D, scale, causal ? 1 : 0};
-  if ((st = launched(nss::launch_bwd_dq(a, (hipStream_t)stream))) != ATTN_OK) return st;
-  return launched(nss::launch_bwd_dkdv(a, (hipStream_t)stream));
+                 void* dq, void* dk, void* dv, float* delta, void* workspace, size_t workspace_bytes, int B, int H,
+                 int N, int D, float scale, int causal, int stabilise, float beta, void* stream) {
+  return bwd_entry(q, k, v, o32, true, dO, lse, dq, dk, dv, delta, workspace, workspace_bytes, B, H, N, D, scale,
+                   causal, stabilise, beta, stream);
 }
 
 }  // extern "C"

@@ -39,13 +39,13 @@ def test_exports_every_header_function():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5, -6, -7, -9, -10):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10):
         assert binding.status_string(s) and binding.status_string(s) != "unknown attn_status"
     assert binding.status_string(12345) == "unknown attn_status"
     # the shape status names the limits the check enforces (N and the launch grid)
     shape_text = binding.status_string(-2)
     assert "2^24" in shape_text and "ceil(N/128)" in shape_text and "2^31" not in shape_text
-    assert binding.abi_version() == 3
+    assert binding.abi_version() == 4
 
 
 def fwd(**kw):
@@ -58,11 +58,12 @@ def fwd(**kw):
 
 def bwd(**kw):
     a = dict(q=addr(0), k=addr(1), v=addr(2), o=addr(3), dO=addr(4), lse=addr(5), dq=addr(6), dk=addr(7),
-             dv=addr(8), delta=addr(9), B=1, H=2, N=64, D=64, scale=0.125, causal=1, stab=1, beta=2.0)
+             dv=addr(8), delta=addr(9), ws=addr(10), wsb=1 << 40, B=1, H=2, N=64, D=64, scale=0.125, causal=1,
+             stab=1, beta=2.0)
     a.update(kw)
     return lib().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["dO"], a["lse"], a["dq"], a["dk"], a["dv"],
-                          a["delta"], a["B"], a["H"], a["N"], a["D"], a["scale"], a["causal"], a["stab"],
-                          a["beta"], None)
+                          a["delta"], a["ws"], a["wsb"], a["B"], a["H"], a["N"], a["D"], a["scale"], a["causal"],
+                          a["stab"], a["beta"], None)
 
 
 def tie(**kw):
@@ -157,8 +158,9 @@ def test_fp32_o_entries_validation():
     bad = list(base)
     bad[5] = addr(4) + 4096
     assert L.attn_fwd_o32(*bad) == -7          # lse inside o32 (fp32: twice the bf16 bytes)
-    # attn_bwd_o32(q, k, v, o32, dO, lse, dq, dk, dv, delta, B, H, N, D, scale, causal, stab, beta, stream)
-    b = [addr(i) for i in range(10)] + [1, 2, 64, 64, 0.125, 1, 1, 2.0, None]
+    # attn_bwd_o32(q, k, v, o32, dO, lse, dq, dk, dv, delta, ws, ws_bytes, B, H, N, D, scale, causal, stab,
+    #              beta, stream)
+    b = [addr(i) for i in range(11)] + [1 << 26, 1, 2, 64, 64, 0.125, 1, 1, 2.0, None]
     bad = list(b)
     bad[3] = None
     assert L.attn_bwd_o32(*bad) == -1
@@ -166,6 +168,20 @@ def test_fp32_o_entries_validation():
     bad[6] = addr(3) + 16
     assert L.attn_bwd_o32(*bad) == -7          # dq inside o32
     bad = list(b)
-    bad[13] = 80
+    bad[15] = 80
     assert L.attn_bwd_o32(*bad) == -3
-    assert L.attn_bwd_o32(*(b[:10] + [0] + b[11:])) == 0   # empty problem
+    bad = list(b)
+    bad[10], bad[11] = None, 0
+    assert L.attn_bwd_o32(*bad) == -9          # no workspace needed: stops at the device check
+    assert L.attn_bwd_o32(*(b[:12] + [0] + b[13:])) == 0   # empty problem
+
+
+def test_workspace_size_and_validation():
+    L = lib()
+    # the backward needs no workspace: 0 for every shape, valid or not
+    for shape in ((2, 3, 100, 64), (2, 3, 100, 128), (0, 3, 100, 64), (1, 1, 64, 96), (-1, 1, 64, 64)):
+        assert L.attn_bwd_workspace_bytes(*shape) == 0
+    # NULL with 0 bytes, or any buffer, passes validation (stops at the device check here)
+    assert bwd(ws=None, wsb=0) == -9
+    assert bwd(D=128, ws=None, wsb=0) == -9
+    assert bwd(ws=addr(10) + 8, wsb=4) == -9
