@@ -68,6 +68,25 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}), flush=True)
 
 
+def settle_clock(dev, seconds: float = 0.1) -> dict:
+    """Untimed GPU load before the warm-up steps: an idle MI355X needs tens
+    of milliseconds of load to reach its working clock (a loop of this step
+    from idle ran its first ~20 ms about 10 % slow), longer than a few warm-up
+    steps of ~0.1 ms take.  The load is bf16 GEMMs of unrelated data (torch),
+    not steps of the workload: nothing they compute reaches the timed steps."""
+    import torch
+    a = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            a = (a @ a) * (1.0 / 64.0)
+        torch.cuda.synchronize()
+        n += 4
+    return {"seconds": round(time.perf_counter() - t0, 3), "gemms": n,
+            "what": "untimed bf16 4096^3 GEMMs of unrelated data before the warm-up steps"}
+
+
 def kernel_hash() -> str:
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
 
@@ -134,6 +153,7 @@ def main():
         bwd_dq()
         bwd_dkdv()
 
+    settled = settle_clock(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -225,6 +245,7 @@ def main():
                    "global_batch": B, "seq_len": N,
                    "parallelism": "none (1 GPU)"},
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "clock_settle": settled,
         "peak_assumption": "2516.6 TFLOPS dense bf16 = 256 CU x 4096 flop/clk x 2.4 GHz",
         "kernels_us": us,
         "fwd_us": us["fwd"],
