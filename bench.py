@@ -76,6 +76,8 @@ def settle_clock(dev, seconds: float = 0.1) -> dict:
     not steps of the workload: nothing they compute reaches the timed steps."""
     import torch
     a = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+    a = (a @ a) * (1.0 / 64.0)  # the GEMM library's own set-up, outside the settle time
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     n = 0
     while time.perf_counter() - t0 < seconds:
