@@ -634,7 +634,13 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
     const void* __restrict__ Og, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
     uint16_t* __restrict__ dQ, float* __restrict__ DELTA, int BH, int N, float scale, int nqt) {
   constexpr int BM = 128, NKB = BN / 32, NKK = D / 16, NCB = D / 32, TILE = BN * D;
+  // STAGE: the workgroup's Q and dO rows come in through LDS (48 KB per
+  // workgroup at d = 64, still three per CU); at d = 128 the two stages alone
+  // take 64 KB and the rows are loaded straight into registers
+  constexpr bool STAGE = D == 64 && !O32;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t qst[STAGE ? BM * D : 8];
+  __shared__ float dlt[STAGE ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -657,25 +663,72 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
 
   bf16x8 qf[NKK], gf[NKK];
   float dl = 0.f;
+  const u32x4 z{0, 0, 0, 0};
+  if constexpr (STAGE) {
+    // The operand layout puts 32 rows in every 16-byte load (lane l: row l %
+    // 32), so a prologue loading Q, dO and O that way moves 32-byte pieces of
+    // 96 rows per instruction.  Instead Q and dO go to LDS as whole rows (the
+    // key tiles' loads: eight lanes per 128-byte row), into a tile of their
+    // own and into the second key stage, which the loop first fills at its
+    // first tile; O is loaded as whole rows too, for delta only (lane l: row
+    // 8i + l/8 of the wave's 32, columns 8(l%8)..+7).
+    uint16_t* const dst = lds + 2 * TILE;
+    tile_to_lds<BM, D>(Q + head, q0, N, qst, wu, lane);
+    tile_to_lds<BM, D>(dO + head, q0, N, dst, wu, lane);
+    const uint16_t* O = static_cast<const uint16_t*>(Og);
+    bf16x8 oc[4];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const size_t off = head + (size_t)qi * D + 16 * kk + 8 * h;
-    const u32x4 z{0, 0, 0, 0};
-    qf[kk] = as_bf16x8(qi < N ? ld16(Q + off) : z);
-    gf[kk] = as_bf16x8(qi < N ? ld16(dO + off) : z);
-    if constexpr (O32) {  // delta from O before its bf16 rounding
-      const float* o32 = static_cast<const float*>(Og) + off;
-      const f32x4 a = qi < N ? *reinterpret_cast<const f32x4*>(o32) : f32x4{};
-      const f32x4 b = qi < N ? *reinterpret_cast<const f32x4*>(o32 + 4) : f32x4{};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dl += (float)gf[kk][e] * a[e] + (float)gf[kk][e + 4] * b[e];
-    } else {
-      const bf16x8 of = as_bf16x8(qi < N ? ld16(static_cast<const uint16_t*>(Og) + off) : z);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dl += (float)gf[kk][e] * (float)of[e];
+    for (int i = 0; i < 4; ++i) {
+      const int r = qw + 8 * i + (lane >> 3);
+      oc[i] = as_bf16x8(r < N ? ld16(O + head + (size_t)r * D + 8 * (lane & 7)) : z);
     }
+    wait_vmem();
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qf[kk] = Tile<D>::row8(qst, 32 * wu + li, 2 * kk + h);
+      gf[kk] = Tile<D>::row8(dst, 32 * wu + li, 2 * kk + h);
+    }
+    // delta_r = sum_c dO_rc O_rc: eight products per lane, then the sum over
+    // the row's eight lanes, handed to the row's lane through LDS
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * wu + 8 * i + (lane >> 3);
+      const bf16x8 g = Tile<D>::row8(dst, r, lane & 7);
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p = __builtin_fmaf((float)g[e], (float)oc[i][e], p);
+      p += __shfl_xor(p, 1);
+      p += __shfl_xor(p, 2);
+      p += __shfl_xor(p, 4);
+      if ((lane & 7) == 0) dlt[r] = p;
+    }
+    dl = dlt[32 * wu + li];
+    if (qi >= N) {  // rows past N: the loads above read row N - 1 there
+      dl = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) qf[kk] = gf[kk] = as_bf16x8(z);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const size_t off = head + (size_t)qi * D + 16 * kk + 8 * h;
+      qf[kk] = as_bf16x8(qi < N ? ld16(Q + off) : z);
+      gf[kk] = as_bf16x8(qi < N ? ld16(dO + off) : z);
+      if constexpr (O32) {  // delta from O before its bf16 rounding
+        const float* o32 = static_cast<const float*>(Og) + off;
+        const f32x4 a = qi < N ? *reinterpret_cast<const f32x4*>(o32) : f32x4{};
+        const f32x4 b = qi < N ? *reinterpret_cast<const f32x4*>(o32 + 4) : f32x4{};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dl += (float)gf[kk][e] * a[e] + (float)gf[kk][e + 4] * b[e];
+      } else {
+        const bf16x8 of = as_bf16x8(qi < N ? ld16(static_cast<const uint16_t*>(Og) + off) : z);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dl += (float)gf[kk][e] * (float)of[e];
+      }
+    }
+    dl = sum32(dl);
   }
-  dl = sum32(dl);
   const float lse2 = qi < N ? LSE[(size_t)bh * N + qi] * kLog2e : 0.f;
   if (h == 0 && qi < N) DELTA[(size_t)bh * N + qi] = dl;
 
