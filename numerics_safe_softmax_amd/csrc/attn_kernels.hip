@@ -310,13 +310,28 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
     if constexpr (!TIES_ONLY) tile_to_lds<BN, D, kFwdSW>(V + head, kt * BN, N, base + TILE, wu, lane);
   };
   bf16x8 qf[NKK];
+  if constexpr (!TIES_ONLY) {
+    // Q's rows come in through the second LDS stage (the loop first fills it
+    // at tile 1) as whole rows, beside the first KV tile's loads, instead of
+    // 32 rows per 16-byte load in the operand layout and before them
+    static_assert(NS == 2 && NT * TILE == BM * D, "one stage holds the Q tile");
+    fetch(0, 0);  // nkt >= 1: the workgroup's first query row is below N
+    uint16_t* const qs = lds + NT * TILE;
+    tile_to_lds<BM, D, kFwdSW>(Q + head, q0, N, qs, wu, lane);  // rows past N: row N - 1
+    wait_vmem();
+    __syncthreads();
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
-    qf[kk] = as_bf16x8(qi < N ? ld16(Q + head + (size_t)qi * D + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
-  wait_vmem();
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[kk] = qi < N ? Tile<D, kFwdSW>::row8(qs, 32 * wu + li, 2 * kk + h) : as_bf16x8(u32x4{0, 0, 0, 0});
+  } else {
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
-    if (st < nkt) fetch(st, st);
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[kk] = as_bf16x8(qi < N ? ld16(Q + head + (size_t)qi * D + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
+    wait_vmem();
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+      if (st < nkt) fetch(st, st);
+  }
 
   f32x16 oacc[NCB];
 #pragma unroll
@@ -519,13 +534,19 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kern
     tile_to_lds<BN, D, kFwdSW>(K + head, kt * BN, N, base, wu, lane);
     tile_to_lds<BN, D, kFwdSW>(V + head, kt * BN, N, base + TILE, wu, lane);
   };
-  bf16x8 qf[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
-    qf[kk] = as_bf16x8(qi < N ? ld16(Q + head + (size_t)qi * D + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
+  // Q's rows through the second LDS stage as whole rows, as in fwd_kernel
   const float m2 = qi < N ? LSE[row] : 0.f;
-  wait_vmem();
   fetch(0, 0);
+  bf16x8 qf[NKK];
+  {
+    uint16_t* const qs = lds + 2 * TILE;
+    tile_to_lds<BM, D, kFwdSW>(Q + head, q0, N, qs, wu, lane);  // rows past N: row N - 1
+    wait_vmem();
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[kk] = qi < N ? Tile<D, kFwdSW>::row8(qs, 32 * wu + li, 2 * kk + h) : as_bf16x8(u32x4{0, 0, 0, 0});
+  }
 
   f32x16 oacc[NCB];
 #pragma unroll
