@@ -291,6 +291,9 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
   constexpr int NS = 2;                   // LDS stages: tiles in flight = NS - 1
   constexpr int LOADS = NT * (TILE / 8 / 256);  // 16-byte loads per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t lds[NS * NT * TILE];
+  // QIN: one stage holds the workgroup's Q tile (every forward; the tie-count
+  // pass with 128-key tiles)
+  constexpr bool QIN = NT * TILE >= BM * D;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -309,12 +312,13 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
     tile_to_lds<BN, D, kFwdSW>(K + head, kt * BN, N, base, wu, lane);
     if constexpr (!TIES_ONLY) tile_to_lds<BN, D, kFwdSW>(V + head, kt * BN, N, base + TILE, wu, lane);
   };
+  static_assert(NS == 2, "the loop is written for two stages");
   bf16x8 qf[NKK];
-  if constexpr (!TIES_ONLY) {
-    // Q's rows come in through the second LDS stage (the loop first fills it
-    // at tile 1) as whole rows, beside the first KV tile's loads, instead of
-    // 32 rows per 16-byte load in the operand layout and before them
-    static_assert(NS == 2 && NT * TILE == BM * D, "one stage holds the Q tile");
+  if constexpr (QIN) {
+    // Q's rows come in through the second stage (the loop first fills it at
+    // tile 1) as whole rows, beside the first KV tile's loads, instead of 32
+    // rows per 16-byte load in the operand layout and before them (a Q tile
+    // of its own for the 64-key tie-count pass measured slower)
     fetch(0, 0);  // nkt >= 1: the workgroup's first query row is below N
     uint16_t* const qs = lds + NT * TILE;
     tile_to_lds<BM, D, kFwdSW>(Q + head, q0, N, qs, wu, lane);  // rows past N: row N - 1
@@ -328,9 +332,7 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
     for (int kk = 0; kk < NKK; ++kk)
       qf[kk] = as_bf16x8(qi < N ? ld16(Q + head + (size_t)qi * D + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
     wait_vmem();
-#pragma unroll
-    for (int st = 0; st < NS - 1; ++st)
-      if (st < nkt) fetch(st, st);
+    fetch(0, 0);
   }
 
   f32x16 oacc[NCB];
