@@ -234,6 +234,22 @@ __device__ __forceinline__ void tile_to_lds(const uint16_t* __restrict__ src, in
   }
 }
 
+// Dispatch order of a forward grid that is resident all at once: the
+// dispatcher places workgroups L, L + 256, L + 512, ... on one CU (seen in
+// per-wave traces of the hardware CU id), so the first band of 256 keeps the
+// heaviest-first order and every later band runs in reverse, by groups of 8
+// so that each head stays on its XCD: the CUs that hold the heaviest causal
+// query tiles, whose chains set the forward's span, get the lightest
+// partners (gpt2_small online forward 29.3 -> 28.4 us, exact final shift
+// 41.7 -> 39.2 us; gpt2_medium within noise; the dQ pass measured unchanged).
+__device__ __forceinline__ int band_order(int L, int G) {
+  constexpr int NCU = 256;
+  if (L < NCU) return L;
+  const int base = L - L % NCU;
+  const int ng = min(NCU, G - base) >> 3, g = (L - base) >> 3;
+  return base + 8 * (ng - 1 - g) + (L & 7);
+}
+
 // Workgroup L -> (tile rank, head).  Workgroups are dispatched to the 8 XCDs
 // round-robin (L % 8); with B*H a multiple of 8 every tile of head bh runs on
 // XCD bh % 8.  Rank 0 is dispatched first.
@@ -299,7 +315,9 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, h = lane >> 5;
   int rank, bh;
-  map_block(blockIdx.x, BH, rank, bh);
+  // the whole grid resident at once (NSS_FWD_WGS workgroups per CU at d = 64, 2 at d = 128)
+  const bool band = CAUSAL && (BH & 7) == 0 && (int)gridDim.x <= 256 * (D == 64 ? NSS_FWD_WGS : 2);
+  map_block(band ? band_order(blockIdx.x, gridDim.x) : (int)blockIdx.x, BH, rank, bh);
   const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
   const size_t head = (size_t)bh * N * D;
   const int q0 = qt * BM, qw = q0 + 32 * wu, qi = qw + li;
@@ -522,7 +540,9 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kern
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, h = lane >> 5;
   int rank, bh;
-  map_block(blockIdx.x, BH, rank, bh);
+  // the whole grid resident at once (NSS_FWD_WGS workgroups per CU at d = 64, 2 at d = 128)
+  const bool band = CAUSAL && (BH & 7) == 0 && (int)gridDim.x <= 256 * (D == 64 ? NSS_FWD_WGS : 2);
+  map_block(band ? band_order(blockIdx.x, gridDim.x) : (int)blockIdx.x, BH, rank, bh);
   const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
   const size_t head = (size_t)bh * N * D;
   const int q0 = qt * BM, qw = q0 + 32 * wu, qi = qw + li;
