@@ -697,6 +697,19 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
 
   const int kend = CAUSAL ? min(q0 + BM, N) : N;
   const int nkt = (kend + BN - 1) / BN;
+  // Staggered start (causal, the whole grid resident at once): every
+  // workgroup loads its rows at the same time, and the first tile is ready
+  // only when most of those bytes have arrived.  The workgroups of lighter
+  // query tiles therefore wait before their first loads, one step per rank
+  // below the heaviest, a step of about the time one rank's rows take to load
+  // (BH * 128 rows * 6d bytes of Q, dO and O at ~5 TB/s: BH * d / 128 units of
+  // s_sleep's 64 clocks), so that the heaviest tiles, whose chains set the
+  // pass's span, get the start-up bandwidth (gpt2_small dQ 30.9 -> 29.9 us;
+  // steps of 2/3 and 4/3 of that gained less, twice it lost).
+  if (CAUSAL && (int)gridDim.x <= (D == 64 ? 768 : 512)) {
+    const int units = (nqt - 1 - qt) * ((BH * D) >> 7);
+    for (int i = 0; i < units; i += 8) __builtin_amdgcn_s_sleep(8);
+  }
   auto fetch = [&](int kt, int buf) {
     uint16_t* base = lds + buf * 2 * TILE;
     tile_to_lds<BN, D>(K + head, kt * BN, N, base, wu, lane);
