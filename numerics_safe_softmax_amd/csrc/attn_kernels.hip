@@ -325,6 +325,14 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
 
   const int kend = CAUSAL ? min(q0 + BM, N) : N;
   const int nkt = (kend + BN - 1) / BN;
+  // Staggered start of the tie-count pass (as in the dQ pass, a step of about
+  // one rank's Q rows at ~5 TB/s: BH * d / 384 units of 64 clocks): the
+  // exact-final-shift forward at gpt2_small 38.2 -> 36.9 us; the online
+  // forward, whose tiles also carry the softmax, measured 0.9 us slower with it
+  if (TIES_ONLY && band) {
+    const int units = (nqt - 1 - qt) * ((BH * D) / 384);
+    for (int i = 0; i < units; i += 8) __builtin_amdgcn_s_sleep(8);
+  }
   auto fetch = [&](int kt, int buf) {
     uint16_t* base = lds + buf * NT * TILE;
     tile_to_lds<BN, D, kFwdSW>(K + head, kt * BN, N, base, wu, lane);
