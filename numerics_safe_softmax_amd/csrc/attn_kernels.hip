@@ -22,8 +22,16 @@
 //   * tiles go global -> LDS directly (global_load_lds_dwordx4, no staging
 //     registers) into an XOR-swizzled row-major layout, double-buffered, one
 //     barrier per tile; rows past N are clamped to row N-1 and masked;
+//   * the rows a workgroup keeps in registers for the whole loop (Q; Q and
+//     dO; K and V) come in the same way, as whole rows, and are read from LDS
+//     in the operand layout (loaded straight in that layout, every 16-byte
+//     load would touch 32 rows);
 //   * all tiles of one (b, h) run on one XCD (its L2 keeps the head's
-//     operands) and causal work is ordered heaviest tile first.
+//     operands) and causal work is ordered heaviest tile first; where a
+//     causal grid is resident all at once, the forward reverses its later
+//     dispatch bands (the CUs of the heaviest tiles get the lightest
+//     partners) and the dQ and tie-count passes start the lighter tiles later
+//     (the heaviest get the start-up bandwidth).
 //
 // MFMA 32x32x16 lane layout (lane l, half h = l / 32):
 //   A (32 x 16): lane l holds row l % 32, k = 8h .. 8h+7
