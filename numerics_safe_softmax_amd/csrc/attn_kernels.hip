@@ -28,10 +28,10 @@
 //     load would touch 32 rows);
 //   * all tiles of one (b, h) run on one XCD (its L2 keeps the head's
 //     operands) and causal work is ordered heaviest tile first; where a
-//     causal grid is resident all at once, the forward reverses its later
-//     dispatch bands (the CUs of the heaviest tiles get the lightest
-//     partners) and the dQ and tie-count passes start the lighter tiles later
-//     (the heaviest get the start-up bandwidth).
+//     causal grid is resident all at once, the forward and the dQ pass
+//     reverse their later dispatch bands (the CUs of the heaviest tiles get
+//     the lightest partners) and the dQ and tie-count passes start the
+//     lighter tiles later (the heaviest get the start-up bandwidth).
 //
 // MFMA 32x32x16 lane layout (lane l, half h = l / 32):
 //   A (32 x 16): lane l holds row l % 32, k = 8h .. 8h+7
@@ -242,14 +242,15 @@ __device__ __forceinline__ void tile_to_lds(const uint16_t* __restrict__ src, in
   }
 }
 
-// Dispatch order of a forward grid that is resident all at once: the
+// Dispatch order of a causal grid that is resident all at once: the
 // dispatcher places workgroups L, L + 256, L + 512, ... on one CU (seen in
 // per-wave traces of the hardware CU id), so the first band of 256 keeps the
 // heaviest-first order and every later band runs in reverse, by groups of 8
 // so that each head stays on its XCD: the CUs that hold the heaviest causal
 // query tiles, whose chains set the forward's span, get the lightest
 // partners (gpt2_small online forward 29.3 -> 28.4 us, exact final shift
-// 41.7 -> 39.2 us; gpt2_medium within noise; the dQ pass measured unchanged).
+// 41.7 -> 39.2 us, gpt2_medium within noise; dQ pass with its staggered start
+// 31.1 -> 30.4 us).
 __device__ __forceinline__ int band_order(int L, int G) {
   constexpr int NCU = 256;
   if (L < NCU) return L;
@@ -705,7 +706,9 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, h = lane >> 5;
   int rank, bh;
-  map_block(blockIdx.x, BH, rank, bh);
+  // the whole grid resident at once: 3 workgroups per CU at d = 64, 2 at d = 128
+  const bool resident = CAUSAL && (int)gridDim.x <= (D == 64 ? 768 : 512);
+  map_block(resident && (BH & 7) == 0 ? band_order(blockIdx.x, gridDim.x) : (int)blockIdx.x, BH, rank, bh);
   const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
   const size_t head = (size_t)bh * N * D;
   const int q0 = qt * BM, qw = q0 + 32 * wu, qi = qw + li;
@@ -722,7 +725,7 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
   // s_sleep's 64 clocks), so that the heaviest tiles, whose chains set the
   // pass's span, get the start-up bandwidth (gpt2_small dQ 30.9 -> 29.9 us;
   // steps of 2/3 and 4/3 of that gained less, twice it lost).
-  if (CAUSAL && (int)gridDim.x <= (D == 64 ? 768 : 512)) {
+  if (resident) {
     const int units = (nqt - 1 - qt) * ((BH * D) >> 7);
     for (int i = 0; i < units; i += 8) __builtin_amdgcn_s_sleep(8);
   }
