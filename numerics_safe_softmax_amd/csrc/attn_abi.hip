@@ -120,7 +120,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   const Span out[] = {{o, tb}, {lse, rb}, {ties, rb}, {pbar_one, rb}, {formed_ones, rb}};
   if ((st = check_alias(in, 3, out, 5)) != ATTN_OK) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  nss::FwdArgs a{q, k, v, o, nullptr, lse, ties, pbar_one, formed_ones, nullptr, nullptr, B, H, N, D, scale,
+  nss::FwdArgs a{q, k, v, o, nullptr, lse, ties, pbar_one, formed_ones, nullptr, B, H, N, D, scale,
                  causal ? 1 : 0, stabilise, beta};
   return launched(nss::launch_fwd(a, (hipStream_t)stream));
 }
@@ -140,7 +140,7 @@ int attn_fwd_o32(const void* q, const void* k, const void* v, void* o, float* o3
   const Span out[] = {{o, tb}, {o32, 2 * tb}, {lse, rb}, {ties, rb}, {pbar_one, rb}, {formed_ones, rb}};
   if ((st = check_alias(in, 3, out, 6)) != ATTN_OK) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  nss::FwdArgs a{q, k, v, o, o32, lse, ties, pbar_one, formed_ones, nullptr, nullptr, B, H, N, D, scale,
+  nss::FwdArgs a{q, k, v, o, o32, lse, ties, pbar_one, formed_ones, nullptr, B, H, N, D, scale,
                  causal ? 1 : 0, stabilise, beta};
   return launched(nss::launch_fwd(a, (hipStream_t)stream));
 }
@@ -158,7 +158,7 @@ int attn_tiecount(const void* q, const void* k, int32_t* ties, float* rowmax, in
   const Span out[] = {{ties, rb}, {rowmax, rb}};
   if ((st = check_alias(in, 2, out, 2)) != ATTN_OK) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  nss::FwdArgs a{q, k, nullptr, nullptr, nullptr, nullptr, ties, nullptr, nullptr, rowmax, nullptr, B, H, N, D,
+  nss::FwdArgs a{q, k, nullptr, nullptr, nullptr, nullptr, ties, nullptr, nullptr, rowmax, B, H, N, D,
                  scale, causal ? 1 : 0, 0, 2.f};
   return launched(nss::launch_tiecount(a, (hipStream_t)stream));
 }

@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ O32, float* __restrict__ LSE, int32_t* __restrict__ TIES,
     int32_t* __restrict__ PONE, int32_t* __restrict__ FORMED, float* __restrict__ ROWMAX,
-    float* __restrict__ SHIFT, int BH, int N, float scale, int stabilise, float beta, int nqt) {
+    int BH, int N, float scale, int stabilise, float beta, int nqt) {
   using F = Fwd<D, BN, CAUSAL, TIES_ONLY>;
   constexpr int BM = F::BM, NKB = F::NKB, NKK = F::NKK, NCB = F::NCB, TILE = F::TILE;
   constexpr int NT = TIES_ONLY ? 1 : 2;  // K (and V) per stage
@@ -334,10 +334,11 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
 
   const int kend = CAUSAL ? min(q0 + BM, N) : N;
   const int nkt = (kend + BN - 1) / BN;
-  // Staggered start of the tie-count pass (as in the dQ pass, a step of about
-  // one rank's Q rows at ~5 TB/s: BH * d / 384 units of 64 clocks): the
-  // exact-final-shift forward at gpt2_small 38.2 -> 36.9 us; the online
-  // forward, whose tiles also carry the softmax, measured 0.9 us slower with it
+  // Staggered start of the duplicate detector (as in the dQ pass, a step of
+  // about one rank's Q rows at ~5 TB/s: BH * d / 384 units of 64 clocks):
+  // attn_tiecount at gpt2_small 15.2 -> 14.8 us, gpt2_medium 17.8 -> 16.3 us;
+  // the online forward, whose tiles also carry the softmax, measured 0.9 us
+  // slower with it, and the fused exact-final-shift forward gained nothing
   if (TIES_ONLY && band) {
     const int units = (nqt - 1 - qt) * ((BH * D) / 384);
     for (int i = 0; i < units; i += 8) __builtin_amdgcn_s_sleep(8);
@@ -493,12 +494,6 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
     if (h == 0 && qi < N) {
       if (TIES) TIES[row] = c_run;
       if (ROWMAX) ROWMAX[row] = scale * m_run;
-      if (SHIFT || PONE) {  // first pass of the exact-final-shift forward
-        const float base = m_run * t;
-        const float m2 = shifted(m_run, c_run, base, stabilise, beta);
-        if (SHIFT) SHIFT[row] = m2;
-        if (PONE) PONE[row] = (__builtin_bit_cast(uint16_t, (__bf16)exp2f_fast(base - m2)) == 0x3F80) ? 1 : 0;
-      }
     }
   } else {
     const float ltot = sum32(lsum);
@@ -535,21 +530,24 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Forward with the final shift known (second pass of the exact-final-shift
-// mode).  The first pass (fwd_kernel<..., TIES_ONLY>) has merged every KV tile
-// of each row into its final (max, count) and stored the shift m2 of the rule
-// in LSE[row] (log2-scaled units); here every P_bar entry is formed once, with
-// that shift, so no entry of a repeated-max row is ever rounded to 1 -- not
-// even transiently, as in the online kernel when a duplicate arrives in a later
-// tile -- and no rescaling is needed.  LSE[row] is then overwritten with the
-// natural-log log-sum-exp.
+// The exact-final-shift forward, both passes in one workgroup.  Pass 1
+// streams K alone and merges every key tile of each row into its final
+// (max, count) (the same merge as fwd_kernel's), from which the rule gives
+// the shift m2 (kept in a register; ties and pbar_one are written here).
+// Pass 2 streams K and V again and forms every P_bar entry once, with that
+// shift, so no entry of a repeated-max row is ever rounded to 1 -- not even
+// transiently, as in the online kernel when a duplicate arrives in a later
+// tile -- and no rescaling is needed.  One kernel instead of a detector pass
+// and a second forward: one start-up and one causal tail fewer, and no shift
+// through HBM (gpt2_small 35.3 -> 31.4 us, gpt2_medium 40.6 -> 38.0 us, sink
+// 85.5 -> 82.0 us; outputs bit-identical, the merge being exact and
+// order-free).
 // ---------------------------------------------------------------------------
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, int BN1>
 __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ O32, float* __restrict__ LSE, int32_t* __restrict__ FORMED, int BH,
-    int N, float scale,
-    int nqt) {
+    uint16_t* __restrict__ O, float* __restrict__ O32, float* __restrict__ LSE, int32_t* __restrict__ FORMED,
+    int32_t* __restrict__ TIES, int32_t* __restrict__ PONE, int BH, int N, float scale, float beta, int nqt) {
   constexpr int BM = 128, NKB = BN / 32, NKK = D / 16, NCB = D / 32, TILE = BN * D;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];
 
@@ -574,8 +572,14 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kern
     tile_to_lds<BN, D, kFwdSW>(V + head, kt * BN, N, base + TILE, wu, lane);
   };
   // Q's rows through the second LDS stage as whole rows, as in fwd_kernel
-  const float m2 = qi < N ? LSE[row] : 0.f;
-  fetch(0, 0);
+  // pass 1 streams K alone, in tiles of BN1 keys (a stage holds 2 BN keys)
+  static_assert(BN1 <= 2 * BN, "a pass-1 key tile fits one stage");
+  constexpr int NKB1 = BN1 / 32;
+  const int nkt1 = (kend + BN1 - 1) / BN1;
+  auto fetch_k = [&](int kt, int buf) {
+    tile_to_lds<BN1, D, kFwdSW>(K + head, kt * BN1, N, lds + buf * 2 * TILE, wu, lane);
+  };
+  fetch_k(0, 0);
   bf16x8 qf[NKK];
   {
     uint16_t* const qs = lds + 2 * TILE;
@@ -586,6 +590,75 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kern
     for (int kk = 0; kk < NKK; ++kk)
       qf[kk] = qi < N ? Tile<D, kFwdSW>::row8(qs, 32 * wu + li, 2 * kk + h) : as_bf16x8(u32x4{0, 0, 0, 0});
   }
+  // pass 1: the whole row's (max, count) over the key tiles, then the rule's
+  // shift from it (the same merge as fwd_kernel's)
+  float m_run = -INFINITY;
+  int c_run = 0;
+  auto tile1 = [&](const int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < nkt1) fetch_k(kt + 1, buf ^ 1);
+    const uint16_t* Kt = lds + buf * 2 * TILE;
+    const int k0 = kt * BN1;
+    const bool active = qw < N && (!CAUSAL || k0 <= qw + 31);
+    if (!active) return;
+    f32x16 s[NKB1];
+    __builtin_amdgcn_iglp_opt(1);
+#pragma unroll
+    for (int kb = 0; kb < NKB1; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < NKB1; ++kb)
+        s[kb] = mfma(Tile<D, kFwdSW>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
+    if ((CAUSAL && k0 + BN1 - 1 > qw) || k0 + BN1 > N) {
+#pragma unroll
+      for (int kb = 0; kb < NKB1; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if ((CAUSAL && key > qi) || key >= N) s[kb][r] = -INFINITY;
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < NKB1; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    int cnt = 0;
+#pragma unroll
+    for (int kb = 0; kb < NKB1; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cnt += (s[kb][r] == mx) ? 1 : 0;
+    {
+      uint32_t ma, mb, ca, cb;
+      swap_halves(__builtin_bit_cast(uint32_t, mx), ma, mb);
+      swap_halves((uint32_t)cnt, ca, cb);
+      const float fa = __builtin_bit_cast(float, ma), fb = __builtin_bit_cast(float, mb);
+      mx = fmaxf(fa, fb);
+      cnt = (fa == mx ? (int)ca : 0) + (fb == mx ? (int)cb : 0);
+    }
+    if (mx == -INFINITY) cnt = 0;
+    if (mx > m_run) {
+      m_run = mx;
+      c_run = cnt;
+    } else if (mx == m_run) {
+      c_run += cnt;
+    }
+  };
+  for (int kt = 0; kt < nkt1; kt += 2) {
+    tile1(kt, IntC<0>{});
+    if (kt + 1 < nkt1) tile1(kt + 1, IntC<1>{});
+  }
+  const float base = m_run * t;
+  const float m2 = qi < N ? shifted(m_run, c_run, base, 1, beta) : 0.f;
+  if (h == 0 && qi < N) {
+    if (TIES) TIES[row] = c_run;
+    if (PONE) PONE[row] = (__builtin_bit_cast(uint16_t, (__bf16)exp2f_fast(base - m2)) == 0x3F80) ? 1 : 0;
+  }
+  __syncthreads();  // every wave is done with the last key tile: pass 2 reloads the stages
+  fetch(0, 0);
 
   f32x16 oacc[NCB];
 #pragma unroll
@@ -1142,7 +1215,7 @@ static hipError_t launch_fwd_bn(const FwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   hipLaunchKernelGGL((fwd_kernel<D, BN, CAUSAL, TIES_ONLY>), dim3(nqt * BH), dim3(256), 0, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.o32,
-                     a.lse, a.ties, a.pbar_one, a.formed_ones, a.rowmax, a.shift, BH, a.N, a.scale, a.stabilise,
+                     a.lse, a.ties, a.pbar_one, a.formed_ones, a.rowmax, BH, a.N, a.scale, a.stabilise,
                      a.beta, nqt);
   return hipGetLastError();
 }
@@ -1164,9 +1237,15 @@ template <int D, bool CAUSAL>
 static hipError_t launch_fwd_fixed_t(const FwdArgs& a, hipStream_t st) {
   const int nqt = (a.N + 127) / 128;
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((fwd_fixed_kernel<D, kFwdBN, CAUSAL>), dim3(nqt * BH), dim3(256), 0, st,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.o32,
-                     a.lse, a.formed_ones, BH, a.N, a.scale, nqt);
+  // pass 1 (K alone) in 128-key tiles from N = 2048 on, as the stand-alone detector
+  if (a.N >= 2048)
+    hipLaunchKernelGGL((fwd_fixed_kernel<D, kFwdBN, CAUSAL, 2 * kFwdBN>), dim3(nqt * BH), dim3(256), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.o32,
+                       a.lse, a.formed_ones, a.ties, a.pbar_one, BH, a.N, a.scale, a.beta, nqt);
+  else
+    hipLaunchKernelGGL((fwd_fixed_kernel<D, kFwdBN, CAUSAL, kFwdBN>), dim3(nqt * BH), dim3(256), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.o32,
+                       a.lse, a.formed_ones, a.ties, a.pbar_one, BH, a.N, a.scale, a.beta, nqt);
   return hipGetLastError();
 }
 
@@ -1178,18 +1257,8 @@ static hipError_t launch_fwd_any(const FwdArgs& a, hipStream_t st) {
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   if (a.stabilise != 2) return launch_fwd_any<false>(a, st);
-  // exact final shift: pass 1 merges each whole row into (max, count) and
-  // stores the rule's shift in LSE (plus ties and pbar_one); pass 2 forms
-  // P_bar once with that shift.
-  FwdArgs p1 = a;
-  p1.o = nullptr;
-  p1.o32 = nullptr;
-  p1.formed_ones = nullptr;
-  p1.rowmax = nullptr;
-  p1.shift = a.lse;
-  p1.stabilise = 1;
-  hipError_t e = launch_fwd_any<true>(p1, st);
-  if (e != hipSuccess) return e;
+  // exact final shift: one kernel, the row's (max, count) first, then P_bar
+  // formed once with the rule's shift
   if (a.D == 64) return a.causal ? launch_fwd_fixed_t<64, true>(a, st) : launch_fwd_fixed_t<64, false>(a, st);
   return a.causal ? launch_fwd_fixed_t<128, true>(a, st) : launch_fwd_fixed_t<128, false>(a, st);
 }

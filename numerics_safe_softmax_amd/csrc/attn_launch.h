@@ -13,7 +13,6 @@ struct FwdArgs {
   float* lse;
   int32_t *ties, *pbar_one, *formed_ones;
   float* rowmax;
-  float* shift;  // first pass of the exact-final-shift mode: the rule's shift per row
   int B, H, N, D;
   float scale;
   int causal, stabilise;  // stabilise: 0 plain, 1 online duplicate-max shift, 2 exact final shift
