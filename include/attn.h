@@ -76,7 +76,7 @@ enum {
   ATTN_PLAIN = 0,        /* plain safe softmax: shift = running row max              */
   ATTN_STAB_ONLINE = 1,  /* duplicate-max shift from the running (max, count)        */
   ATTN_STAB_EXACT = 2    /* duplicate-max shift from the whole row's final (max,     */
-                         /* count): two passes, no transient P_bar == 1              */
+                         /* count): two passes over the keys, no transient P_bar == 1 */
 };
 
 /*
@@ -114,9 +114,10 @@ enum {
  *                occurrence leaves one transient exact 1 in P_bar (rescaled
  *                away afterwards; counted in formed_ones).
  *                ATTN_STAB_EXACT (2): the duplicate-max shift from each row's
- *                final (max, count): a first pass merges every KV tile of the
- *                row (it writes ties and pbar_one, and keeps the shift in lse),
- *                the second pass forms every P_bar entry once with that shift,
+ *                final (max, count): one launch, in which each workgroup
+ *                first merges every KV tile of its rows (writing ties and
+ *                pbar_one; the shift stays on chip), then forms every P_bar
+ *                entry once with that shift,
  *                so no entry of a repeated-max row ever equals 1 (the rule of
  *                the minimal-fix section applied to the whole row, as written),
  *                and formed_ones counts exactly the entries whose bf16 rounding
