@@ -19,9 +19,10 @@
 //     bf16 B operand of the next (P_bar V, dS K, P^T dO, dS^T Q): the k index
 //     of each MFMA is permuted to match, and the other operand is read
 //     transposed out of the row-major LDS tile with ds_read_b64_tr_b16;
-//   * tiles go global -> LDS directly (global_load_lds_dwordx4, no staging
-//     registers) into an XOR-swizzled row-major layout, double-buffered, one
-//     barrier per tile; rows past N are clamped to row N-1 and masked;
+//   * tiles go global -> LDS directly (buffer_load_dwordx4 ... lds, no
+//     staging registers) into an XOR-swizzled row-major layout,
+//     double-buffered, one barrier per tile; rows past N are clamped to row
+//     N-1 and masked;
 //   * the rows a workgroup keeps in registers for the whole loop (Q; Q and
 //     dO; K and V) come in the same way, as whole rows, and are read from LDS
 //     in the operand layout (loaded straight in that layout, every 16-byte
@@ -225,11 +226,24 @@ struct Tile {
 // Rows [r0, r0+R) of a bf16 [N][D] matrix straight into a swizzled LDS tile;
 // every thread of the 256 issues (R*D/8)/256 16-byte loads.  Rows past N read
 // row N-1 (finite data; the kernels mask them).
+//
+// The loads are buffer_load_dwordx4 ... lds through a resource over the one
+// head's matrix (src, N*D*2 bytes: below 2^32 since N < 2^24 and D <= 128, so
+// a 32-bit byte offset reaches every row).  The global_load_lds form of the
+// same transfer is a FLAT instruction to the compiler, which then cannot
+// count LDS reads while a prefetch is in flight and waits for all of them
+// (lgkmcnt(0)) before every use; with the buffer form its waits are exact.
+// Measured on MI355X, outputs bit-identical: gpt2_small dK/dV 39.7 -> 39.1 us,
+// forward 27.4 -> 26.6 us, exact-shift forward 32.0 -> 30.4 us; gpt2_medium
+// dK/dV 51.3 -> 48.1 us; sink and long_context backward -3 %.
 template <int R, int D, int SW = 1>
 __device__ __forceinline__ void tile_to_lds(const uint16_t* __restrict__ src, int r0, int N, uint16_t* tile,
                                             int wu, int lane) {
   constexpr int CPR = D / 8, TOT = R * CPR, PER = TOT / 256;
   static_assert(TOT % 256 == 0, "tile must be a whole number of workgroup loads");
+  // dword 3: 32-bit data format, no swizzle, no index stride (raw byte offsets)
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)((uint32_t)N * (uint32_t)D * 2u), 0x00020000);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int P = i * 256 + wu * 64 + lane;
@@ -237,8 +251,8 @@ __device__ __forceinline__ void tile_to_lds(const uint16_t* __restrict__ src, in
     const int c = p ^ Tile<D, SW>::swz(r);
     int gr = r0 + r;
     gr = gr < N ? gr : N - 1;
-    __builtin_amdgcn_global_load_lds(src + (size_t)gr * D + c * 8, (lds_void*)(tile + (i * 256 + wu * 64) * 8), 16,
-                                     0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (i * 256 + wu * 64) * 8), 16,
+                                             (int)((uint32_t)(gr * D + c * 8) * 2u), 0, 0, 0);
   }
 }
 
