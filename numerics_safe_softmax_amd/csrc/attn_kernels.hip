@@ -935,6 +935,11 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16 s = f32x16{}, dp = negd;
+      // scheduling hint for the block's MFMA / LDS / vector interleave at
+      // d = 64 (measured: gpt2_medium dQ 38.7 -> 37.8 us, sink 70.3 -> 69.8
+      // us, gpt2_small within noise; long_context, d = 128, 374 -> 377 us, so
+      // not there; outputs bit-identical)
+      if constexpr (D == 64) __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         s = mfma(Tile<D>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s);
