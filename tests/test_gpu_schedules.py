@@ -2,12 +2,15 @@
 
 When a causal grid is resident all at once, the forward and the dQ pass
 reorder their workgroups (later dispatch bands reversed by groups of 8) and
-the dQ and tie-count passes start the lighter query tiles later.  These cases
-build grids that take those paths (B*H a multiple of 8 with more than 256
-workgroups, partial bands, ragged N, d = 64 and 128, and a grid whose B*H is
-not a multiple of 8), fill every output with NaN first so that a tile the
-reordered grid skipped would show, and compare sampled heads with the oracle
-(every head has query tiles in the reversed bands)."""
+the dQ and tie-count passes start the lighter query tiles later; where the
+key tiles of an XCD exceed one round of the dK/dV pass (more than 64), its
+workgroups take heavy + light pairs of key tiles.  These cases build grids
+that take those paths (B*H a multiple of 8 with more than 256 workgroups,
+partial bands, ragged N, d = 64 and 128, paired key tiles with and without an
+odd count, and a grid whose B*H is not a multiple of 8), fill every output
+with NaN first so that a tile the reordered grid skipped would show, and
+compare sampled heads with the oracle (every head has query tiles in the
+reversed bands)."""
 import numpy as np
 import pytest
 
@@ -26,6 +29,8 @@ CASES = [
     (1, 96, 650, 64, 73),     # 576: three bands, the last partial; ragged
     (1, 48, 1000, 128, 74),   # 384 at d = 128 (resident up to 512)
     (3, 5, 1500, 64, 75),     # B*H = 15: the stagger without the band order
+    (1, 24, 5400, 64, 76),    # dK/dV pairing: 129 key tiles per XCD (odd), one taken alone
+    (1, 40, 1700, 128, 77),   # dK/dV pairing at d = 128: 70 key tiles per XCD
 ]
 
 
