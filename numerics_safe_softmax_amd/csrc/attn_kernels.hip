@@ -987,18 +987,28 @@ __global__ __launch_bounds__(256, NSS_DQ_WAVES) void bwd_dq_kernel(
 //
 // Causal grids with more key tiles per XCD than its CUs hold at once (two
 // workgroups per CU) are packed into one such round: with `single` >= 0, the
-// local workgroup j of an XCD takes the XCD's j-th heaviest key tile and, from
-// j = single on, after it the lightest one not yet taken, so the heavy tiles
-// run alone and the rest in heavy + light pairs of about equal length
-// (gpt2_small dK/dV 39.9 -> 39.5 us, gpt2_medium 49.2 -> 48.2 us; sink and
-// long_context within noise; outputs bit-identical).  Each key tile is
-// computed exactly as by a workgroup of its own.
+// first `single` workgroups of an XCD take its heaviest key tiles alone and
+// the others a heavy + light pair each (the tiles single + p and nloc - 1 - p),
+// and the launcher places the pairs so that the CUs' work evens out and the
+// two workgroups of a CU share a head where they can (gpt2_small dK/dV 39.9
+// -> 39.5 us for the pairing, then 38.6 -> 37.6 us for the placement, two
+// boxes; gpt2_medium 49.2 -> 48.2 us; sink and long_context within noise;
+// outputs bit-identical).  Each key tile is computed exactly as by a
+// workgroup of its own.
 // ---------------------------------------------------------------------------
+// Which pair of key tiles each paired workgroup of an XCD's round takes (see
+// launch_dkdv_t): slot s (workgroup single + s of the XCD) takes pair p[s],
+// i.e. the XCD's key tiles single + p[s] and nloc - 1 - p[s].  Passed by value.
+struct PairOrder {
+  uint8_t p[64];
+};
+
 template <int D, int BQ, bool CAUSAL>
 __global__ __launch_bounds__(256, NSS_DKDV_WAVES) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale, int nkt, int single) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale, int nkt, int single,
+    PairOrder ord) {
   constexpr int BK = 128, NQB = BQ / 32, NKK = D / 16, NCB = D / 32, TILE = BQ * D;
   // d = 128: the workgroup's V rows sit in LDS (32 KB) and are read as the dP
   // products' B operand where used, instead of 32 VGPRs per lane: the kernel
@@ -1028,10 +1038,15 @@ __global__ __launch_bounds__(256, NSS_DKDV_WAVES) void bwd_dkdv_kernel(
   const int li = lane & 31, h = lane >> 5;
   // the workgroup's key tiles (linear indices as map_block takes them; index
   // L runs on XCD L % 8, so both tiles of a pair belong to this XCD)
-  int item1 = -1;
+  int item0 = blockIdx.x, item1 = -1;
   if (CAUSAL && single >= 0) {
-    const int jl = blockIdx.x >> 3, nloc = (BH >> 3) * nkt;
-    if (jl >= single) item1 = 8 * (nloc - 1 - (jl - single)) + (blockIdx.x & 7);
+    const int jl = blockIdx.x >> 3, nloc = (BH >> 3) * nkt, x = blockIdx.x & 7;
+    if (jl >= single) {
+      // one round (nloc <= 128): the pair the launcher placed on this slot
+      const int pr = nloc <= 128 ? (int)ord.p[jl - single] : jl - single;
+      item0 = 8 * (single + pr) + x;
+      item1 = 8 * (nloc - 1 - pr) + x;
+    }
   }
   auto body = [&](const int L) {
   int rank, bh;
@@ -1249,7 +1264,7 @@ __global__ __launch_bounds__(256, NSS_DKDV_WAVES) void bwd_dkdv_kernel(
                    dva[cb][4 * g + 3]);
     }
   };
-  body(blockIdx.x);
+  body(item0);
   if constexpr (CAUSAL) {
     if (item1 >= 0) {
       __syncthreads();  // the next key tile's prologue rewrites the LDS
@@ -1338,6 +1353,67 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Placement of the paired key tiles of one XCD's round of 64 workgroups (nloc
+// key tiles, heaviest first, the XCD's key tile l being key tile l / hx of its
+// head l % hx; nqt query tiles per head, qpk query tiles per key tile).  The
+// dispatcher puts workgroups L and L + 256 on one CU, i.e. workgroups j and
+// j + 32 of an XCD.  Each key tile costs its query tiles plus one for its
+// prologue.  CUs are taken heaviest first (by the single key tile they hold)
+// and each free pair slot gets the cheapest pair left; among equal ones, a
+// pair whose first key tile has the head of the CU's other work (the two
+// workgroups then stream the same Q and dO rows at about the same time, so
+// they meet in the XCD's L2), and among those the slot's own pair.  Measured
+// against the plain order (slot s takes pair s): gpt2_small dK/dV 38.6 ->
+// 37.6 us (a balanced order without the head rule: 38.4 -> 38.3 us); the
+// GPT-2 medium and long-context grids (equal pairs, already head-aligned)
+// keep the plain order.
+static void place_pairs(PairOrder& ord, int nloc, int single, int hx, int nqt, int qpk) {
+  auto cost = [&](int l) { return nqt - (l / hx) * qpk + 1; };
+  const int npairs = (nloc - single) / 2;  // = 64 - single
+  auto pcost = [&](int q) { return cost(single + q) + cost(nloc - 1 - q); };
+  int fixed[32] = {}, fhead[32], nfree[32] = {}, freeslot[32][2], cu[32];
+  bool used[64] = {};
+  for (int c = 0; c < 32; ++c) fhead[c] = -1;
+  for (int j = 0; j < 64; ++j) {
+    const int c = j & 31;
+    if (j < single) {
+      fixed[c] += cost(j);
+      if (fhead[c] < 0) fhead[c] = j % hx;
+    } else {
+      freeslot[c][nfree[c]++] = j - single;
+    }
+  }
+  for (int c = 0; c < 32; ++c) cu[c] = c;
+  for (int i = 1; i < 32; ++i)  // CUs by fixed work, heaviest first (stable)
+    for (int k = i; k > 0 && fixed[cu[k]] > fixed[cu[k - 1]]; --k) {
+      const int tmp = cu[k];
+      cu[k] = cu[k - 1];
+      cu[k - 1] = tmp;
+    }
+  for (int i = 0; i < 32; ++i) {
+    const int c = cu[i];
+    for (int f = 0; f < nfree[c]; ++f) {
+      const int slot = freeslot[c][f];
+      int mc = -1;
+      for (int q = 0; q < npairs; ++q)
+        if (!used[q] && (mc < 0 || pcost(q) < mc)) mc = pcost(q);
+      int pick = -1, rank_best = 4;  // every candidate ranks 0..3
+      for (int q = 0; q < npairs; ++q) {
+        if (used[q] || pcost(q) != mc) continue;
+        const bool aligned = fhead[c] < 0 || (single + q) % hx == fhead[c];
+        const int rank = (aligned ? 0 : 2) + (q == slot ? 0 : 1);
+        if (rank < rank_best) {
+          rank_best = rank;
+          pick = q;
+        }
+      }
+      used[pick] = true;
+      ord.p[slot] = (uint8_t)pick;
+      if (fhead[c] < 0) fhead[c] = (single + pick) % hx;
+    }
+  }
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   constexpr int BQ = (D == 64 ? NSS_DKDV_BQ : 32);
@@ -1347,6 +1423,7 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   // CU (32 CUs per XCD) where they exceed it; nloc - single is made even so
   // that the paired tiles pair up exactly
   int grid = nkt * BH, single = -1;
+  PairOrder ord{};
   if (CAUSAL && (BH & 7) == 0) {
     const int nloc = (BH >> 3) * nkt, per_round = 64;
     if (nloc > per_round) {
@@ -1354,11 +1431,12 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
       if ((nloc - sg) & 1) ++sg;
       single = sg;
       grid = 8 * (sg + (nloc - sg) / 2);
+      if (nloc <= 2 * per_round) place_pairs(ord, nloc, sg, BH >> 3, (a.N + BQ - 1) / BQ, 128 / BQ);
     }
   }
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, CAUSAL>), dim3(grid), dim3(256), 0, st, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.delta,
-                     (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.N, a.scale, nkt, single);
+                     (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.N, a.scale, nkt, single, ord);
   return hipGetLastError();
 }
 
