@@ -39,12 +39,19 @@ def _same(a, b):
     return torch.equal(a, b)
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2])
-def test_graph_replays_match_eager(mode):
+# (B, H, N, D, modes): a small grid in every mode, and a grid whose dK/dV key
+# tiles are paired and placed (72 key tiles per XCD; the placement is a
+# by-value kernel argument, copied into the graph at capture)
+GRAPH_CASES = [(1, 8, 640, 64, m) for m in (0, 1, 2)] + [(1, 96, 650, 64, 1)]
+
+
+@pytest.mark.parametrize("case", GRAPH_CASES, ids=lambda c: "B%dH%dN%dD%d_m%d" % c)
+def test_graph_replays_match_eager(case):
     import numerics_safe_softmax_amd as nss
-    w = inputs.custom("graph", 1, 8, 640, 64, True, 31, tie_block=8, v_skew_dims=16, v_mu=-2.0, v_sigma=0.5,
+    B, H, N, D, mode = case
+    w = inputs.custom("graph", B, H, N, D, True, 31, tie_block=8, v_skew_dims=16, v_mu=-2.0, v_sigma=0.5,
                       do_mu=-0.5)
-    print("graph mode %d" % mode, flush=True)
+    print("graph %s" % (case,), flush=True)
     t = parity.to_dev(inputs.generate(w), DEV)
     eager = _buffers(t["q"])
     graph = _buffers(t["q"])
