@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 METRIC = "causal attn fwd+bwd TFLOPS (bf16) at GPT-2 shape; % of MFMA peak; O/dP signed bias"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk/CU x 2.4 GHz, dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "numerics_safe_softmax_amd", "csrc", "attn_kernels.hip")
+KERNEL_SOURCE_DIR = os.path.join(ROOT, "numerics_safe_softmax_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2_small.md")
 
 
@@ -90,7 +90,14 @@ def settle_clock(dev, seconds: float = 0.1) -> dict:
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) over the files of the kernel source
+    directory in name order, each as its file name followed by its bytes: the
+    kernels, the launchers and the schedule helpers."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCE_DIR)):
+        h.update(name.encode())
+        h.update(open(os.path.join(KERNEL_SOURCE_DIR, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str):
@@ -99,7 +106,7 @@ def measured_traffic(kernel: str):
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
-    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m = re.search(r"csrc_sha256_16:\s*([0-9a-f]+)", text)
     if not m or m.group(1) != kernel_hash():
         return None
     m = re.search(r"^%s_bytes_per_launch:\s*([0-9.eE+]+)" % re.escape(kernel), text, re.M)
