@@ -164,6 +164,50 @@ def test_long_row_tiecount_and_exact_shift(case):
         parity.check_forward(f2, ref2, rows_mask=m.reshape(w.B, w.H, w.N), label="long rows %s" % (case,))
 
 
+# Attention-sink rows: key 0 is every row's maximum from the first tile on and
+# three exact copies of it sit further along, so most later tiles hold no
+# value that reaches a row's running maximum (the forward skips their count,
+# merge and rescale for the whole wave) while the tiles with a copy must add
+# to the count.  N >= 2048 takes the 128-key detector tiles as well.
+SINK = [
+    (1, 2, 700, 64, False, 41),
+    (1, 2, 600, 128, True, 42),
+    (1, 1, 2100, 64, False, 43),
+]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", SINK, ids=lambda c: "B%dH%dN%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
+def test_sink_rows_parity(case, mode):
+    import numerics_safe_softmax_amd as nss
+    B, H, N, D, causal, seed = case
+    w = inputs.custom("sink_rows", B, H, N, D, causal, seed, sink=True, v_skew_dims=D // 2, v_mu=-2.0,
+                      v_sigma=0.5, do_mu=-0.5)
+    _say("sink rows %s mode=%d" % (case, mode))
+    d = inputs.generate(w)
+    t = parity.to_dev(d, DEV)
+    f = parity.gpu_forward(t, w, mode)
+    b = parity.gpu_backward(t, w, f, mode)
+    r = nss.tiecount(t["q"], t["k"], scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    ref = oracle.forward(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, stabilise=mode != 0,
+                         beta=w.beta)
+    rb = oracle.backward(d["q"], d["k"], d["v"], d["dO"], ref, scale=w.scale, causal=w.causal)
+    with parity.record_on_failure("sink_%s_m%d" % (case, mode), d, w, mode):
+        fr = parity.check_forward(f, ref, label=str(case))
+        br = parity.check_backward(b, rb, label=str(case))
+        _say("  fwd %s bwd %s" % (fr, br))
+        ok = ref["amb_tie"] == 0
+        ties = r["ties"].cpu().numpy()
+        assert np.array_equal(ties[ok], ref["ties"][ok])
+        assert np.array_equal(ties, f["ties"].cpu().numpy())
+        # the workload does what it is for: repeated maxima on most rows
+        assert np.mean(ref["ties"] > 1) > 0.5
+        if mode:
+            okp = (ref["ties"] > 1) & ok & (ref["amb_pbar"] == 0) & ((ref["flags"] & 1) == 0)
+            assert np.all(f["pbar_one"].cpu().numpy()[okp] == 0)
+
+
 def test_deterministic_reruns():
     w = _small_workload(2, 2, 700, 64, True, 21, 7)
     d = inputs.generate(w)
