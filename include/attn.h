@@ -229,6 +229,19 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
 int attn_tiecount(const void* q, const void* k, int32_t* ties, float* rowmax,
                   int B, int H, int N, int D, float scale, int causal, void* stream);
 
+/*
+ * attn_fwd_key_tile -- keys per KV tile of attn_fwd and attn_fwd_o32 for head
+ * size D: 64 at D = 64, 32 at D = 128; ATTN_E_HEADDIM for any other D.  No
+ * device call.  The online modes (ATTN_PLAIN, ATTN_STAB_ONLINE) merge the
+ * running (max, count) and move the shift once per tile (the rule of
+ * itsolotime.com/archives/23922, section "极简修复方案", applied to the running
+ * pair of the tiled computation that 91haoming.cn/news/show-608006 describes
+ * in section 三), so which P_bar entries are transiently formed as 1
+ * (formed_ones) depends on this width; ATTN_STAB_EXACT and every other output
+ * (up to rounding) do not.
+ */
+int attn_fwd_key_tile(int D);
+
 /* Static, human-readable text for an attn_status value. */
 const char* attn_status_string(int status);
 

@@ -8,8 +8,8 @@ generates the seeded synthetic workloads.
 """
 from .binding import (AttnError, abi_version, attn_bwd, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_o32,
                       attn_bwd_workspace_bytes, attn_fwd, attn_fwd_o32, attn_tiecount, backward, forward,
-                      status_string, tiecount, workspace_for)
+                      fwd_key_tile, status_string, tiecount, workspace_for)
 
 __all__ = ["AttnError", "abi_version", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_o32",
            "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_o32", "attn_tiecount", "backward", "forward",
-           "status_string", "tiecount", "workspace_for"]
+           "fwd_key_tile", "status_string", "tiecount", "workspace_for"]

@@ -33,6 +33,7 @@ _SIGS = {
     "attn_tiecount": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P],
     "attn_status_string": [_I],
     "attn_abi_version": [],
+    "attn_fwd_key_tile": [_I],
 }
 
 
@@ -74,6 +75,14 @@ def status_string(status: int) -> str:
 
 def abi_version() -> int:
     return int(lib().attn_abi_version())
+
+
+def fwd_key_tile(D: int) -> int:
+    """Keys per KV tile of the forward for head size D (the online modes'
+    tile-by-tile shift depends on it)."""
+    w = int(lib().attn_fwd_key_tile(int(D)))
+    _check(min(w, 0))
+    return w
 
 
 def _check(rc: int) -> None:

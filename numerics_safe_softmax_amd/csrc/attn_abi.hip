@@ -86,7 +86,12 @@ int launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_DEVICE; }
 
 extern "C" {
 
-int attn_abi_version(void) { return 4; }
+int attn_abi_version(void) { return 5; }
+
+int attn_fwd_key_tile(int D) {
+  const int w = nss::fwd_key_tile(D);
+  return w > 0 ? w : ATTN_E_HEADDIM;
+}
 
 const char* attn_status_string(int status) {
   switch (status) {

@@ -80,6 +80,10 @@
 #ifndef NSS_FWD_SWZ
 #define NSS_FWD_SWZ 0
 #endif
+// keys per KV tile of the D = 64 forward (64 or 128)
+#ifndef NSS_FWD_BN
+#define NSS_FWD_BN 64
+#endif
 
 namespace nss {
 
@@ -95,6 +99,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kFwdSW = NSS_FWD_SWZ;
+// Keys per KV tile of the forwards.  D = 128 streams 32-key tiles: two LDS
+// stages then take 32 KB and the kernel 164 VGPRs, so three workgroups (3
+// waves per SIMD) fit on a CU instead of two with 64-key tiles (long_context
+// online forward 341 -> 321 us, plain 339 -> 318, exact final shift 427 ->
+// 410 on one box).  The online modes apply the shift tile by tile, so the
+// width is part of what they compute (attn_fwd_key_tile reports it).
+template <int D>
+constexpr int kFwdTile = D == 64 ? NSS_FWD_BN : 32;
+// workgroups per CU the forwards are compiled for (launch bounds and the
+// resident-grid test of the band order)
+template <int D, int BN>
+constexpr int kFwdWgs = D == 64 ? NSS_FWD_WGS : (BN == 32 ? 3 : 2);
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // bf16 rounds x to exactly 1.0 (nearest even) iff 1 - 2^-9 <= x <= 1 + 2^-8;
@@ -333,7 +349,7 @@ struct Fwd {
 };
 
 template <int D, int BN, bool CAUSAL, bool TIES_ONLY>
-__global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
+__global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ O32, float* __restrict__ LSE, int32_t* __restrict__ TIES,
     int32_t* __restrict__ PONE, int32_t* __restrict__ FORMED, float* __restrict__ ROWMAX,
@@ -352,8 +368,8 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, h = lane >> 5;
   int rank, bh;
-  // the whole grid resident at once (NSS_FWD_WGS workgroups per CU at d = 64, 2 at d = 128)
-  const bool band = CAUSAL && (BH & 7) == 0 && (int)gridDim.x <= 256 * (D == 64 ? NSS_FWD_WGS : 2);
+  // the whole grid resident at once
+  const bool band = CAUSAL && (BH & 7) == 0 && (int)gridDim.x <= 256 * kFwdWgs<D, BN>;
   map_block(band ? band_order(blockIdx.x, gridDim.x) : (int)blockIdx.x, BH, rank, bh);
   const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
   const size_t head = (size_t)bh * N * D;
@@ -584,7 +600,7 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_kernel(
 // order-free).
 // ---------------------------------------------------------------------------
 template <int D, int BN, bool CAUSAL, int BN1>
-__global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kernel(
+__global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_fixed_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ O32, float* __restrict__ LSE, int32_t* __restrict__ FORMED,
     int32_t* __restrict__ TIES, int32_t* __restrict__ PONE, int BH, int N, float scale, float beta, int nqt) {
@@ -595,8 +611,8 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kern
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, h = lane >> 5;
   int rank, bh;
-  // the whole grid resident at once (NSS_FWD_WGS workgroups per CU at d = 64, 2 at d = 128)
-  const bool band = CAUSAL && (BH & 7) == 0 && (int)gridDim.x <= 256 * (D == 64 ? NSS_FWD_WGS : 2);
+  // the whole grid resident at once
+  const bool band = CAUSAL && (BH & 7) == 0 && (int)gridDim.x <= 256 * kFwdWgs<D, BN>;
   map_block(band ? band_order(blockIdx.x, gridDim.x) : (int)blockIdx.x, BH, rank, bh);
   const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
   const size_t head = (size_t)bh * N * D;
@@ -621,7 +637,7 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kern
   };
   fetch_k(0, 0);
   bf16x8 qf[NKK];
-  {
+  if constexpr (2 * TILE >= BM * D) {
     uint16_t* const qs = lds + 2 * TILE;
     tile_to_lds<BM, D, kFwdSW>(Q + head, q0, N, qs, wu, lane);  // rows past N: row N - 1
     wait_vmem();
@@ -629,6 +645,12 @@ __global__ __launch_bounds__(256, D == 64 ? NSS_FWD_WGS : 2) void fwd_fixed_kern
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qf[kk] = qi < N ? Tile<D, kFwdSW>::row8(qs, 32 * wu + li, 2 * kk + h) : as_bf16x8(u32x4{0, 0, 0, 0});
+  } else {
+    // the second stage is smaller than the Q tile (D = 128, 32-key tiles):
+    // the rows go straight into registers
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[kk] = as_bf16x8(qi < N ? ld16(Q + head + (size_t)qi * D + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
   }
   // pass 1: the whole row's (max, count) over the key tiles, then the rule's
   // shift from it (the same merge as fwd_kernel's)
@@ -1298,10 +1320,6 @@ __global__ __launch_bounds__(256, NSS_DKDV_WAVES) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-#ifndef NSS_FWD_BN
-#define NSS_FWD_BN 64
-#endif
-constexpr int kFwdBN = NSS_FWD_BN;  // keys per forward KV tile (64 or 128)
 
 template <int D, int BN, bool CAUSAL, bool TIES_ONLY>
 static hipError_t launch_fwd_bn(const FwdArgs& a, hipStream_t st) {
@@ -1322,22 +1340,26 @@ static hipError_t launch_fwd_bn(const FwdArgs& a, hipStream_t st) {
 // are the same for either width.
 template <int D, bool CAUSAL, bool TIES_ONLY>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  if constexpr (TIES_ONLY)
+  if constexpr (TIES_ONLY) {
     if (a.N >= 2048) return launch_fwd_bn<D, 128, CAUSAL, true>(a, st);
-  return launch_fwd_bn<D, kFwdBN, CAUSAL, TIES_ONLY>(a, st);
+    return launch_fwd_bn<D, 64, CAUSAL, true>(a, st);
+  }
+  return launch_fwd_bn<D, kFwdTile<D>, CAUSAL, false>(a, st);
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_fixed_t(const FwdArgs& a, hipStream_t st) {
   const int nqt = (a.N + 127) / 128;
   const int BH = a.B * a.H;
-  // pass 1 (K alone) in 128-key tiles from N = 2048 on, as the stand-alone detector
+  constexpr int BN = kFwdTile<D>;
+  // pass 1 (K alone) in tiles of twice the width (one stage) from N = 2048 on,
+  // as the stand-alone detector
   if (a.N >= 2048)
-    hipLaunchKernelGGL((fwd_fixed_kernel<D, kFwdBN, CAUSAL, 2 * kFwdBN>), dim3(nqt * BH), dim3(256), 0, st,
+    hipLaunchKernelGGL((fwd_fixed_kernel<D, BN, CAUSAL, 2 * BN>), dim3(nqt * BH), dim3(256), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.o32,
                        a.lse, a.formed_ones, a.ties, a.pbar_one, BH, a.N, a.scale, a.beta, nqt);
   else
-    hipLaunchKernelGGL((fwd_fixed_kernel<D, kFwdBN, CAUSAL, kFwdBN>), dim3(nqt * BH), dim3(256), 0, st,
+    hipLaunchKernelGGL((fwd_fixed_kernel<D, BN, CAUSAL, BN>), dim3(nqt * BH), dim3(256), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.o32,
                        a.lse, a.formed_ones, a.ties, a.pbar_one, BH, a.N, a.scale, a.beta, nqt);
   return hipGetLastError();
@@ -1358,6 +1380,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_tiecount(const FwdArgs& a, hipStream_t st) { return launch_fwd_any<true>(a, st); }
+
+int fwd_key_tile(int D) { return D == 64 ? kFwdTile<64> : D == 128 ? kFwdTile<128> : 0; }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {

@@ -34,5 +34,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_tiecount(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st);
+// keys per KV tile of the forward for head size D (0 for an unsupported D)
+int fwd_key_tile(int D);
 
 }  // namespace nss

@@ -29,7 +29,8 @@ def lib():
 def test_exports_every_header_function():
     names = binding.header_functions()
     assert set(names) >= {"attn_fwd", "attn_bwd", "attn_tiecount", "attn_status_string", "attn_fwd_o32",
-                          "attn_bwd_o32", "attn_bwd_dq", "attn_bwd_dkdv", "attn_abi_version"}
+                          "attn_bwd_o32", "attn_bwd_dq", "attn_bwd_dkdv", "attn_abi_version",
+                          "attn_fwd_key_tile"}
     L = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(L, n), n
@@ -45,7 +46,17 @@ def test_status_strings():
     # the shape status names the limits the check enforces (N and the launch grid)
     shape_text = binding.status_string(-2)
     assert "2^24" in shape_text and "ceil(N/128)" in shape_text and "2^31" not in shape_text
-    assert binding.abi_version() == 4
+    assert binding.abi_version() == 5
+
+
+def test_forward_key_tile():
+    # a pure query (no device call): the forward's KV tile width per head size
+    assert binding.fwd_key_tile(64) == 64
+    assert binding.fwd_key_tile(128) == 32
+    for D in (0, 32, 96, 256, -64):
+        assert lib().attn_fwd_key_tile(D) == -3
+        with pytest.raises(binding.AttnError):
+            binding.fwd_key_tile(D)
 
 
 def fwd(**kw):

@@ -41,6 +41,7 @@ REPORT = {}
 
 @pytest.mark.parametrize("wname,heads", CASES, ids=[c[0] for c in CASES])
 def test_events_and_bias(wname, heads):
+    import numerics_safe_softmax_amd as nss
     w = inputs.WORKLOADS[wname]
     print("bias %s heads %s" % (wname, heads), flush=True)
     d = inputs.generate(w)
@@ -88,7 +89,7 @@ def test_events_and_bias(wname, heads):
         if stabilise in (0, 1):
             # the formed ones, row by row, against the rule applied tile by tile
             on = oracle.online_ones(d["q"], d["k"], scale=w.scale, causal=w.causal, stabilise=stabilise != 0,
-                                    beta=w.beta, tile=64, rows=rows)
+                                    beta=w.beta, tile=nss.fwd_key_tile(w.D), rows=rows)
             dec = rmask & (on["amb"] == 0)
             assert np.array_equal(formed[stabilise][dec], on["ones"][dec])
             rep["online_count_rows_checked"] = int(dec.sum())

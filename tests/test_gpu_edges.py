@@ -209,7 +209,8 @@ def test_tie_positions_within_and_across_tiles(mode, D, causal):
         assert np.array_equal(ties[h][seen], want[seen]), (label, keys)
         assert np.array_equal(ref["ties"][0, h][seen], want[seen])
     if mode == 1:
-        on = oracle.online_ones(q, k, scale=scale, causal=causal, stabilise=True, beta=2.0, tile=64)
+        on = oracle.online_ones(q, k, scale=scale, causal=causal, stabilise=True, beta=2.0,
+                               tile=nss.fwd_key_tile(D))
         ok = on["amb"] == 0
         formed = f["formed_ones"].cpu().numpy()
         assert np.array_equal(formed[ok], on["ones"][ok]), label
@@ -227,7 +228,7 @@ R10_HEADS = [
     ((10, 40), 4.0, 150, 6.0),     # positive: shift 8 -> 6 (alpha = e^(2 scale))
     ((10, 70), 4.0, 150, 7.5),     # the repeat completes in tile 1 (shift up), then down in tile 2
     ((10, 40), -1.0, 150, -0.5),   # negative: shift 0 -> -0.5
-    ((3, 60), -2.0, 100, -1.25),   # negative, overtaken in the next tile
+    ((3, 60), -2.0, 100, -1.25),   # negative, overtaken in the next 64-key tile
 ]
 
 
@@ -272,10 +273,11 @@ def test_online_shift_moves_down(mode, D, causal):
     scale = D ** -0.5
     # the construction: on the rows that see every marked key the running shift
     # rises at the repeat and falls at the overtaking key
+    T = nss.fwd_key_tile(D)
     for h, (reps, a, b, bval) in enumerate(R10_HEADS):
         raw = inputs.bits_to_float(k[0, h, :, 0]).astype(np.float64)
-        sh = _online_shifts(list(raw), beta, 64)
-        assert sh[b // 64] < sh[b // 64 - 1], (h, sh)
+        sh = _online_shifts(list(raw), beta, T)
+        assert sh[b // T] < sh[b // T - 1], (h, sh)
     t = {n: inputs.to_torch(x, DEV) for n, x in (("q", q), ("k", k), ("v", v), ("dO", dO))}
     label = "shift moves down D%d mode %d causal %d" % (D, mode, causal)
     _say(label)
@@ -291,7 +293,8 @@ def test_online_shift_moves_down(mode, D, causal):
         seen_b = np.arange(N) >= bkey if causal else np.ones(N, dtype=bool)
         assert np.all(ties[h][seen_b] == 1), label          # the overtaking key is the single maximum
     if mode in (0, 1):
-        on = oracle.online_ones(q, k, scale=scale, causal=causal, stabilise=mode == 1, beta=beta, tile=64)
+        on = oracle.online_ones(q, k, scale=scale, causal=causal, stabilise=mode == 1, beta=beta,
+                               tile=nss.fwd_key_tile(D))
         ok = on["amb"] == 0
         assert np.array_equal(f["formed_ones"].cpu().numpy()[ok], on["ones"][ok]), label
     else:

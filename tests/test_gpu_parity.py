@@ -83,15 +83,17 @@ def test_small_fwd_bwd_parity(case, mode):
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dH%dN%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
 def test_online_formed_ones(case, mode):
     """The kernel's count of formed bf16 ones equals the oracle's online count
-    (the rule applied to the running pair, 64-key tiles, in key order) on
+    (the rule applied to the running pair, tiles of the forward's width, in key order) on
     every row the oracle can decide: the transient exact 1 of a tie split
     across tiles included, bit for bit."""
+    import numerics_safe_softmax_amd as nss
     w = _small_workload(*case)
     d = inputs.generate(w)
     t = parity.to_dev(d, DEV)
     f = parity.gpu_forward(t, w, mode)
     torch.cuda.synchronize()
-    r = oracle.online_ones(d["q"], d["k"], scale=w.scale, causal=w.causal, stabilise=mode != 0, beta=w.beta, tile=64)
+    r = oracle.online_ones(d["q"], d["k"], scale=w.scale, causal=w.causal, stabilise=mode != 0, beta=w.beta,
+                           tile=nss.fwd_key_tile(w.D))
     ok = r["amb"] == 0
     formed = f["formed_ones"].cpu().numpy()
     bad = int(np.sum(formed[ok] != r["ones"][ok]))
