@@ -360,8 +360,9 @@ __global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_kernel(
   constexpr int NS = 2;                   // LDS stages: tiles in flight = NS - 1
   constexpr int LOADS = NT * (TILE / 8 / 256);  // 16-byte loads per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t lds[NS * NT * TILE];
-  // QIN: one stage holds the workgroup's Q tile (every forward; the tie-count
-  // pass with 128-key tiles)
+  // QIN: one stage holds the workgroup's Q tile (the d = 64 forward and the
+  // tie-count pass with 128-key tiles; the d = 128 forward's 32-key stages are
+  // smaller, and its Q rows go straight into registers)
   constexpr bool QIN = NT * TILE >= BM * D;
 
   const int tid = threadIdx.x, lane = tid & 63;
