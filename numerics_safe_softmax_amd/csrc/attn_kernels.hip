@@ -98,7 +98,12 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kFwdSW = NSS_FWD_SWZ;
+// LDS swizzle of the forwards' tiles: NSS_FWD_SWZ at D = 64, the
+// conflict-free one at D = 128 (its extra address registers still fit three
+// workgroups per CU; long_context exact-shift forward 386 -> 379 us, tie
+// count -1 %, online forward within noise)
+template <int D>
+constexpr int kFwdSW = D == 128 ? 1 : NSS_FWD_SWZ;
 // Keys per KV tile of the forwards.  D = 128 streams 32-key tiles: two LDS
 // stages then take 32 KB and the kernel 164 VGPRs, so three workgroups (3
 // waves per SIMD) fit on a CU instead of two with 64-key tiles (long_context
@@ -390,8 +395,8 @@ __global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_kernel(
   }
   auto fetch = [&](int kt, int buf) {
     uint16_t* base = lds + buf * NT * TILE;
-    tile_to_lds<BN, D, kFwdSW>(K + head, kt * BN, N, base, wu, lane);
-    if constexpr (!TIES_ONLY) tile_to_lds<BN, D, kFwdSW>(V + head, kt * BN, N, base + TILE, wu, lane);
+    tile_to_lds<BN, D, kFwdSW<D>>(K + head, kt * BN, N, base, wu, lane);
+    if constexpr (!TIES_ONLY) tile_to_lds<BN, D, kFwdSW<D>>(V + head, kt * BN, N, base + TILE, wu, lane);
   };
   static_assert(NS == 2, "the loop is written for two stages");
   bf16x8 qf[NKK];
@@ -402,12 +407,12 @@ __global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_kernel(
     // of its own for the 64-key tie-count pass measured slower)
     fetch(0, 0);  // nkt >= 1: the workgroup's first query row is below N
     uint16_t* const qs = lds + NT * TILE;
-    tile_to_lds<BM, D, kFwdSW>(Q + head, q0, N, qs, wu, lane);  // rows past N: row N - 1
+    tile_to_lds<BM, D, kFwdSW<D>>(Q + head, q0, N, qs, wu, lane);  // rows past N: row N - 1
     wait_vmem();
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      qf[kk] = qi < N ? Tile<D, kFwdSW>::row8(qs, 32 * wu + li, 2 * kk + h) : as_bf16x8(u32x4{0, 0, 0, 0});
+      qf[kk] = qi < N ? Tile<D, kFwdSW<D>>::row8(qs, 32 * wu + li, 2 * kk + h) : as_bf16x8(u32x4{0, 0, 0, 0});
   } else {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_kernel(
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = mfma(Tile<D, kFwdSW>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
+        s[kb] = mfma(Tile<D, kFwdSW<D>>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
     if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -530,12 +535,12 @@ __global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_kernel(
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 p0 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 0), p1 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 1);
+        const bf16x8 p0 = pack8<Tile<D, kFwdSW<D>>::SPLIT>(s[kb], 0), p1 = pack8<Tile<D, kFwdSW<D>>::SPLIT>(s[kb], 1);
         lsum_bf = add_bf16x8(p1, add_bf16x8(p0, lsum_bf));
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          oacc[cb] = mfma(Tile<D, kFwdSW>::trans8(Vt, 32 * kb, 0, cb, lane), p0, oacc[cb]);
-          oacc[cb] = mfma(Tile<D, kFwdSW>::trans8(Vt, 32 * kb, 1, cb, lane), p1, oacc[cb]);
+          oacc[cb] = mfma(Tile<D, kFwdSW<D>>::trans8(Vt, 32 * kb, 0, cb, lane), p0, oacc[cb]);
+          oacc[cb] = mfma(Tile<D, kFwdSW<D>>::trans8(Vt, 32 * kb, 1, cb, lane), p1, oacc[cb]);
         }
       }
     }
@@ -625,8 +630,8 @@ __global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_fixed_kernel(
   const int nkt = (kend + BN - 1) / BN;
   auto fetch = [&](int kt, int buf) {
     uint16_t* base = lds + buf * 2 * TILE;
-    tile_to_lds<BN, D, kFwdSW>(K + head, kt * BN, N, base, wu, lane);
-    tile_to_lds<BN, D, kFwdSW>(V + head, kt * BN, N, base + TILE, wu, lane);
+    tile_to_lds<BN, D, kFwdSW<D>>(K + head, kt * BN, N, base, wu, lane);
+    tile_to_lds<BN, D, kFwdSW<D>>(V + head, kt * BN, N, base + TILE, wu, lane);
   };
   // Q's rows through the second LDS stage as whole rows, as in fwd_kernel
   // pass 1 streams K alone, in tiles of BN1 keys (a stage holds 2 BN keys)
@@ -634,18 +639,18 @@ __global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_fixed_kernel(
   constexpr int NKB1 = BN1 / 32;
   const int nkt1 = (kend + BN1 - 1) / BN1;
   auto fetch_k = [&](int kt, int buf) {
-    tile_to_lds<BN1, D, kFwdSW>(K + head, kt * BN1, N, lds + buf * 2 * TILE, wu, lane);
+    tile_to_lds<BN1, D, kFwdSW<D>>(K + head, kt * BN1, N, lds + buf * 2 * TILE, wu, lane);
   };
   fetch_k(0, 0);
   bf16x8 qf[NKK];
   if constexpr (2 * TILE >= BM * D) {
     uint16_t* const qs = lds + 2 * TILE;
-    tile_to_lds<BM, D, kFwdSW>(Q + head, q0, N, qs, wu, lane);  // rows past N: row N - 1
+    tile_to_lds<BM, D, kFwdSW<D>>(Q + head, q0, N, qs, wu, lane);  // rows past N: row N - 1
     wait_vmem();
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      qf[kk] = qi < N ? Tile<D, kFwdSW>::row8(qs, 32 * wu + li, 2 * kk + h) : as_bf16x8(u32x4{0, 0, 0, 0});
+      qf[kk] = qi < N ? Tile<D, kFwdSW<D>>::row8(qs, 32 * wu + li, 2 * kk + h) : as_bf16x8(u32x4{0, 0, 0, 0});
   } else {
     // the second stage is smaller than the Q tile (D = 128, 32-key tiles):
     // the rows go straight into registers
@@ -674,7 +679,7 @@ __global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_fixed_kernel(
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int kb = 0; kb < NKB1; ++kb)
-        s[kb] = mfma(Tile<D, kFwdSW>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
+        s[kb] = mfma(Tile<D, kFwdSW<D>>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
     if ((CAUSAL && k0 + BN1 - 1 > qw) || k0 + BN1 > N) {
 #pragma unroll
       for (int kb = 0; kb < NKB1; ++kb)
@@ -754,7 +759,7 @@ __global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_fixed_kernel(
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = mfma(Tile<D, kFwdSW>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
+        s[kb] = mfma(Tile<D, kFwdSW<D>>::row8(Kt, 32 * kb + li, 2 * kk + h), qf[kk], s[kb]);
     if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -780,12 +785,12 @@ __global__ __launch_bounds__(256, (kFwdWgs<D, BN>)) void fwd_fixed_kernel(
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const bf16x8 p0 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 0), p1 = pack8<Tile<D, kFwdSW>::SPLIT>(s[kb], 1);
+      const bf16x8 p0 = pack8<Tile<D, kFwdSW<D>>::SPLIT>(s[kb], 0), p1 = pack8<Tile<D, kFwdSW<D>>::SPLIT>(s[kb], 1);
       lsum_bf = add_bf16x8(p1, add_bf16x8(p0, lsum_bf));
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        oacc[cb] = mfma(Tile<D, kFwdSW>::trans8(Vt, 32 * kb, 0, cb, lane), p0, oacc[cb]);
-        oacc[cb] = mfma(Tile<D, kFwdSW>::trans8(Vt, 32 * kb, 1, cb, lane), p1, oacc[cb]);
+        oacc[cb] = mfma(Tile<D, kFwdSW<D>>::trans8(Vt, 32 * kb, 0, cb, lane), p0, oacc[cb]);
+        oacc[cb] = mfma(Tile<D, kFwdSW<D>>::trans8(Vt, 32 * kb, 1, cb, lane), p1, oacc[cb]);
       }
     }
   };
