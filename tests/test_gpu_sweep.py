@@ -4,7 +4,8 @@ Each case runs the C-ABI forward and backward and compares them element by
 element with the FP64 oracle (O, LSE, delta, dQ, dK, dV within tolerance;
 duplicate counts and P_bar == 1 flags bit-exact off the rows the oracle marks
 undecidable in fp32).  The boundary lengths straddle the 32-row wave blocks,
-the 64-key / 64-query tiles and the 128-row workgroup tiles of every kernel.
+the 32-, 64- and 128-key / 64-query tiles and the 128-row workgroup tiles of
+every kernel.
 """
 import sys
 
@@ -40,6 +41,9 @@ RANDOM = _random_cases(24, 2026)
 BOUNDARY = [(1, 2, n, 64, True, 2100 + n, 4, 1) for n in (31, 32, 33, 63, 64, 65, 127, 128, 129, 191, 192, 193,
                                                           255, 256, 257)]
 BOUNDARY += [(1, 1, n, 128, False, 2400 + n, 0, 2) for n in (63, 65, 129, 255)]
+# the d = 128 forward's 32-key tiles, online modes, causal and not
+BOUNDARY += [(1, 2, n, 128, True, 2500 + n, 4, 1) for n in (31, 32, 33, 95, 96, 97, 161)]
+BOUNDARY += [(1, 1, n, 128, False, 2600 + n, 0, 0) for n in (33, 97, 160)]
 
 
 def _ident(c):
