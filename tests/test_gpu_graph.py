@@ -43,6 +43,8 @@ def _same(a, b):
 # tiles are paired and placed (72 key tiles per XCD; the placement is a
 # by-value kernel argument, copied into the graph at capture)
 GRAPH_CASES = [(1, 8, 640, 64, m) for m in (0, 1, 2)] + [(1, 96, 650, 64, 1)]
+# d = 128: 32-key forward tiles at three workgroups per CU, 32-query dK/dV tiles
+GRAPH_CASES += [(1, 8, 700, 128, m) for m in (1, 2)]
 
 
 @pytest.mark.parametrize("case", GRAPH_CASES, ids=lambda c: "B%dH%dN%dD%d_m%d" % c)
