@@ -26,7 +26,12 @@
 //   * the rows a workgroup keeps in registers for the whole loop (Q; Q and
 //     dO; K and V) come in the same way, as whole rows, and are read from LDS
 //     in the operand layout (loaded straight in that layout, every 16-byte
-//     load would touch 32 rows);
+//     load would touch 32 rows) in the d = 64 forward, the d = 64 dQ pass and
+//     the causal d = 64 dK/dV pass; the other kernels load them straight
+//     into registers;
+//   * a forward tile in which no lane reaches its row's running maximum
+//     changes neither the (max, count) pair nor the shift, and skips the
+//     count, the merge and the rescale (a wave-uniform test);
 //   * all tiles of one (b, h) run on one XCD (its L2 keeps the head's
 //     operands) and causal work is ordered heaviest tile first; where a
 //     causal grid is resident all at once, the forward and the dQ pass
