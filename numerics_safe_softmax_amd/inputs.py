@@ -161,7 +161,7 @@ def generate(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
     qb, kb, vb, gb = (to_bf16_bits(a) for a in (q, k, v, dO))
     if w.sink:
         for b in range(B):                                    # three copies of the sink key
-            pos = rng.choice(np.arange(1, N), size=3, replace=False)
+            pos = rng.choice(np.arange(1, N), size=min(3, N - 1), replace=False)  # fewer when N < 4
             for j in pos:
                 kb[b, :, j, :] = kb[b, :, 0, :]
     elif w.tie_block and w.causal:
